@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE decode tail on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the whole tail at b=64 tokens, P=3584:
+
+  1. EP finalize of tp=8 simulated ranks' GEMM2 rows (top-16 routes, 2 local
+     per rank) into the resident rank-partial buffer [8, 64, 3584];
+  2. the shared expert 7168 -> 6144 (gate/up, SiLU) -> 7168 into the
+     reduce-scatter partial rs [64, 7168];
+  3. the latent combine of the rank partials, RMSNorm and the 3584 -> 7168 up
+     projection plus rs -> out [64, 7168].
+
+Each step replays a HIP graph of the three calls; two input sets (weights
+and rows) alternate so that the 315 MB of weights per step stream from HBM,
+not from the 256 MB Infinity Cache.  Inputs are resident in HBM before the
+timed region starts.  Rank 0 prints one JSON line (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+B, P, TP, K = 64, 3584, 8, 16
+H, I = 7168, 6144
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes():
+    """Bytes each call must move at least (inputs read once, outputs written
+    once), per entry point of the step."""
+    fin = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2 + TP * B * P * 2
+    shared = 3 * H * I * 2 + B * H * 2 + B * H * 2
+    upproj = TP * B * P * 2 + P * 2 + H * P * 2 + B * H * 2 + B * H * 2
+    return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-config kernel table")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the tp rank partials are a resident buffer on one device).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import expert_finalize_rmsnorm_amd as mt
+    import workloads
+    from tests.gpu_util import dev
+
+    torch.cuda.set_device(0)
+    nsets = 2
+    log("drawing inputs")
+    sets = []
+    for s in range(nsets):
+        ep = workloads.ep_finalize(s, b=B, K=K, P=P, tp=TP)
+        up = workloads.upproj(s, b=B, tp=TP, L=P, N=H)
+        sh = workloads.shared(s, b=B, H=H, I=I)
+        d = dict(rows=dev(ep["rows"]), idx=dev(ep["idx"]), w=dev(ep["w32"]),
+                 gamma=dev(ep["gamma"]), x=dev(sh["x"]), wg=dev(sh["w_gate"]),
+                 wu=dev(sh["w_up"]), wd=dev(sh["w_down"]), lgamma=dev(up["gamma"]),
+                 w_up=dev(up["w_up"]),
+                 lat=torch.empty((TP, B, P), dtype=torch.int16, device="cuda"),
+                 rs=torch.empty((B, H), dtype=torch.int16, device="cuda"),
+                 out=torch.empty((B, H), dtype=torch.int16, device="cuda"),
+                 ws_sh=mt.new_workspace(mt.OP_SHARED_EXPERT, B, H, I),
+                 ws_up=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, B, P, H, TP),
+                 host=(ep, up, sh) if s == 0 else None)
+        sets.append(d)
+    torch.cuda.synchronize()
+
+    def finalize(d):
+        mt.moetail_finalize(d["rows"], d["idx"], d["w"], d["gamma"], 1.0, 1e-6, True,
+                            partials=d["lat"])
+
+    def shared(d):
+        mt.moetail_shared_expert(d["x"], d["wg"], d["wu"], d["wd"], d["rs"], workspace=d["ws_sh"])
+
+    def upproj(d):
+        mt.moetail_combine_norm_upproj(d["lat"], d["lgamma"], 1e-6, d["w_up"], d["out"],
+                                       rs=d["rs"], workspace=d["ws_up"])
+
+    def step(d):
+        finalize(d)
+        shared(d)
+        upproj(d)
+
+    log("capturing the step graphs")
+    for d in sets:
+        step(d)  # eager once before capture
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graphs = []
+    for d in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(d)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    log(f"warmup {args.warmup}, timed {args.steps} steps")
+    for i in range(args.warmup):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        graphs[i % nsets].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = B / (ms_per_step * 1e-3)
+    step_bytes = sum(algorithmic_bytes().values())
+    log(f"step {ms_per_step * 1e3:.1f} us wall, {gpu_ms * 1e3:.1f} us GPU events")
+
+    # Per entry point: eager back-to-back calls on the current stream, HIP
+    # events around each block of calls.
+    def time_calls(fn, reps=20):
+        for i in range(4):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(sets[i % nsets])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps  # us per call
+
+    per_call = {n: time_calls(f) for n, f in
+                (("finalize", finalize), ("shared_expert", shared),
+                 ("combine_norm_upproj", upproj))}
+    algo = algorithmic_bytes()
+    entry = {n: dict(us=round(per_call[n], 2), bytes=algo[n],
+                     GBps=round(algo[n] / per_call[n] / 1e3, 1),
+                     frac=round(algo[n] / per_call[n] / 1e3 / HBM_PEAK_GBPS, 4))
+             for n in per_call}
+    dom = "shared_expert"
+    roofline = dict(bound="hbm", kernel="moetail_shared_expert (gate/up + down), b=64",
+                    achieved=entry[dom]["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=entry[dom]["frac"], traffic=None)
+
+    kernels = None
+    if not args.no_kernels:
+        log("per-config kernel timings")
+        kernels = config_kernels(sets[0], log)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        cpu = cpu_baseline(sets[0]["host"], log)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "config": {"workload": "MoE decode tail step: EP finalize tp=8 K=16 P=3584 -> shared "
+                               "expert 7168x6144 SiLU -> latent combine + RMSNorm + up "
+                               "projection 3584->7168 (+rs)",
+                   "b": B, "P": P, "tp": TP, "K": K, "H": H, "I": I,
+                   "global_batch": B, "parallelism": "one GPU, tp rank partials resident"},
+        "gpu_ms_per_step_events": round(gpu_ms, 5),
+        "step_algorithmic_bytes": step_bytes,
+        "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "entry_points": entry,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def config_kernels(base, log):
+    """Per-config timings on cold inputs: enough distinct input sets rotate
+    that their total exceeds twice the 256 MB Infinity Cache."""
+    import numpy as np
+    import torch
+
+    import expert_finalize_rmsnorm_amd as mt
+    import workloads
+    from tests.gpu_util import dev
+
+    gen = torch.Generator("cuda").manual_seed(1234)
+
+    def randn_bf16(shape, std):
+        return (torch.randn(shape, device="cuda", generator=gen) * std).to(torch.bfloat16).view(
+            torch.int16)
+
+    def timed(fn, nsets, reps=None):
+        reps = reps or max(2 * nsets, 12)
+        for i in range(min(nsets, 4)):
+            fn(i % nsets)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i % nsets)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    res = []
+
+    def add(name, us, nbytes, **extra):
+        gbps = nbytes / us / 1e3
+        res.append(dict(name=name, us=round(us, 2), bytes=nbytes, GBps=round(gbps, 1),
+                        frac=round(gbps / HBM_PEAK_GBPS, 4), **extra))
+        log(f"  {name}: {us:.2f} us, {gbps:.0f} GB/s")
+
+    # EP finalize + rank combine at decode scale (the metric's b=64, P=3584)
+    rows = [randn_bf16((TP, B * K // TP, P), 2.0) for _ in range(48)]
+    part = torch.empty((TP, B, P), dtype=torch.int16, device="cuda")
+    out = torch.empty((B, P), dtype=torch.int16, device="cuda")
+    fin_in = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2
+    for wbn in (True, False):
+        us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], base["gamma"],
+                                                 1.0, 1e-6, wbn, partials=part, out=out), 48)
+        add(f"finalize+combine b=64 P=3584 tp=8 wbn={int(wbn)}", us,
+            fin_in + TP * B * P * 2 + B * P * 2, tokens_per_s=round(B / (us * 1e-6), 1))
+    us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], base["gamma"],
+                                             1.0, 1e-6, True, out=out), 48)
+    add("finalize+combine b=64, out only (partials not written)", us, fin_in + B * P * 2,
+        tokens_per_s=round(B / (us * 1e-6), 1))
+    del rows
+
+    # expert-TP finalize: b=128, K=16, P=7168, tp=8 (235 MB of K-partials)
+    g0 = torch.Generator("cpu").manual_seed(0)
+    w32, _ = workloads.route_weights(g0, 128, 16)
+    tgamma = workloads.normal_bf16(g0, (7168,), 1.0, 0.05)
+    idx = torch.from_numpy(np.random.default_rng(0).permutation(2048).astype(np.int32).reshape(
+        128, 16)).cuda()
+    kp = [randn_bf16((8, 2048, 7168), 0.5) for _ in range(3)]
+    tout = torch.empty((128, 7168), dtype=torch.int16, device="cuda")
+    w, gamma = dev(w32), dev(tgamma)
+    us = timed(lambda i: mt.moetail_tp_finalize(kp[i], idx, w, gamma, 0.0, 1e-6, False, tout), 3,
+               reps=12)
+    add("tp_finalize b=128 K=16 P=7168 tp=8", us,
+        8 * 2048 * 7168 * 2 + 128 * 16 * 8 + 7168 * 2 + 128 * 7168 * 2,
+        tokens_per_s=round(128 / (us * 1e-6), 1))
+    del kp
+
+    # latent combine + norm + up projection, b in {1, 8, 32, 64}
+    wups = [randn_bf16((H, P), 0.02) for _ in range(12)]
+    for b in (1, 8, 32, 64):
+        lat = randn_bf16((TP, b, P), 1.0)
+        o = torch.empty((b, H), dtype=torch.int16, device="cuda")
+        ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, P, H, TP)
+        us = timed(lambda i: mt.moetail_combine_norm_upproj(lat, base["lgamma"], 1e-6, wups[i], o,
+                                                            workspace=ws), 12)
+        add(f"combine_norm_upproj b={b}", us, H * P * 2 + TP * b * P * 2 + P * 2 + b * H * 2,
+            weight_roofline_us=round(H * P * 2 / HBM_PEAK_GBPS / 1e3, 2))
+    del wups
+
+    # shared expert, b in {16, 32, 64, 128}
+    ws_sets = [(randn_bf16((I, H), 0.02), randn_bf16((I, H), 0.02), randn_bf16((H, I), 0.02))
+               for _ in range(2)]
+    for b in (16, 32, 64, 128):
+        x = randn_bf16((b, H), 1.0)
+        rs = torch.empty((b, H), dtype=torch.int16, device="cuda")
+        ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
+        us = timed(lambda i: mt.moetail_shared_expert(x, *ws_sets[i], rs, workspace=ws), 2,
+                   reps=12)
+        add(f"shared_expert b={b}", us, 3 * H * I * 2 + 2 * b * H * 2,
+            weight_roofline_us=round(3 * H * I * 2 / HBM_PEAK_GBPS / 1e3, 2))
+    return res
+
+
+def cpu_baseline(host_inputs, log):
+    """The oracle (as it stands) on the step's full b=64 batch, on host cores."""
+    import numpy as np
+
+    import oracle
+    ep, up, sh = host_inputs
+    threads = max(1, min(16, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    lat, _ = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
+                             combine=False, nthreads=threads)
+    _, rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                 nthreads=threads)
+    oracle.combine_norm_upproj(lat, up["gamma"], 1e-6, up["w_up"], rs, nthreads=threads)
+    dt = time.perf_counter() - t0
+    log(f"oracle step {dt:.2f} s on {threads} threads")
+    del np
+    return {"value": round(B / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full b={B} step (finalize, shared expert, combine+norm+upproj) of "
+                      f"input set 0, {dt:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+"""Python binding of libmoetail: the MoE decode tail on one MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in ``include/moetail.h``: the same
+entry-point names, device tensors in, status codes turned into exceptions.
+Every step of the tail runs in the library's HIP kernels; PyTorch only owns
+device memory and streams.  There is no fallback: if ``libmoetail.so`` is
+missing the import of an entry point raises.
+
+BF16 tensors are ``torch.bfloat16`` (or int16/uint16 views of BF16 bits);
+route weights ``torch.float32`` or ``torch.bfloat16``; indices
+``torch.int32``.  All tensors must be contiguous CUDA (HIP) tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoetail.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT = 0, 1, 2, 3
+
+ENTRY_POINTS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
+                "moetail_shared_expert", "moetail_workspace_bytes", "moetail_status_string")
+
+
+class MoetailError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoetail.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m expert_finalize_rmsnorm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        SZ = ctypes.c_size_t
+        L.moetail_finalize.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, I32, I32, I32,
+                                       P, P, P]
+        L.moetail_tp_finalize.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, I32, I32, I32,
+                                          P, P]
+        L.moetail_combine_norm_upproj.argtypes = [P, I32, P, F, P, I32, P, I32, I32, P, P, P,
+                                                  SZ, P]
+        L.moetail_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, SZ, P]
+        L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+        L.moetail_workspace_bytes.restype = SZ
+        L.moetail_status_string.argtypes = [I32]
+        L.moetail_status_string.restype = ctypes.c_char_p
+        for f in ENTRY_POINTS[:4]:
+            getattr(L, f).restype = I32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moetail_status_string(status).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("libmoetail takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoetail takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _bf16(t, name):
+    if t is not None and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold BF16 bits, got {t.dtype}")
+    return t
+
+
+def _weights(w):
+    if w.dtype == torch.float32:
+        return F32
+    if w.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    raise TypeError("route weights must be float32 or bfloat16")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != OK:
+        raise MoetailError(status, where)
+
+
+def workspace_bytes(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0) -> int:
+    return int(lib().moetail_workspace_bytes(op, b, dim0, dim1, dim2))
+
+
+def moetail_finalize(rows, permuted_idx, route_w, gamma, gain_center, eps, weight_before_norm,
+                     partials=None, out=None, stream=None):
+    """rows [tp, R, P], permuted_idx [tp, b, K], route_w [b, K], gamma [P];
+    writes partials [tp, b, P] and/or out [b, P]."""
+    _bf16(rows, "rows"), _bf16(gamma, "gamma"), _bf16(partials, "partials"), _bf16(out, "out")
+    tp, R, P = rows.shape
+    _, b, K = permuted_idx.shape
+    if permuted_idx.dtype != torch.int32:
+        raise TypeError("permuted_idx must be int32")
+    st = lib().moetail_finalize(_ptr(rows), R, _ptr(permuted_idx), _ptr(route_w),
+                                _weights(route_w), _ptr(gamma), float(gain_center), float(eps),
+                                int(bool(weight_before_norm)), b, K, P, tp, _ptr(partials),
+                                _ptr(out), _stream(stream))
+    _check(st, "moetail_finalize")
+
+
+def moetail_tp_finalize(kpartials, permuted_idx, route_w, gamma, gain_center, eps,
+                        weight_before_norm, out, stream=None):
+    """kpartials [tp, num_rows, P], permuted_idx [b, K], route_w [b, K]; writes out [b, P]."""
+    _bf16(kpartials, "kpartials"), _bf16(gamma, "gamma"), _bf16(out, "out")
+    tp, num_rows, P = kpartials.shape
+    b, K = permuted_idx.shape
+    if permuted_idx.dtype != torch.int32:
+        raise TypeError("permuted_idx must be int32")
+    st = lib().moetail_tp_finalize(_ptr(kpartials), num_rows, _ptr(permuted_idx),
+                                   _ptr(route_w), _weights(route_w), _ptr(gamma),
+                                   float(gain_center), float(eps), int(bool(weight_before_norm)),
+                                   b, K, P, tp, _ptr(out), _stream(stream))
+    _check(st, "moetail_tp_finalize")
+
+
+def moetail_combine_norm_upproj(latent_partials, gamma, eps, w_up, out, rs=None, normed=None,
+                                workspace=None, stream=None):
+    """latent_partials [tp, b, L], gamma [L], w_up [N, L], rs [b, N] or None;
+    writes out [b, N] and normed [b, L] when given.  workspace: a device
+    tensor of at least workspace_bytes(OP_COMBINE_NORM_UPPROJ, b, L, N, tp)
+    bytes."""
+    for t, n in ((latent_partials, "latent_partials"), (gamma, "gamma"), (w_up, "w_up"),
+                 (out, "out"), (rs, "rs"), (normed, "normed")):
+        _bf16(t, n)
+    tp, b, L = latent_partials.shape
+    N = w_up.shape[0]
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moetail_combine_norm_upproj(_ptr(latent_partials), tp, _ptr(gamma), float(eps),
+                                           _ptr(w_up), N, _ptr(rs), b, L, _ptr(normed),
+                                           _ptr(out), ws, wsb, _stream(stream))
+    _check(st, "moetail_combine_norm_upproj")
+
+
+def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, stream=None):
+    """x [b, H], w_gate/w_up [I, H], w_down [H, I]; writes rs [b, H] and h
+    [b, I] when given.  workspace: at least
+    workspace_bytes(OP_SHARED_EXPERT, b, H, I) bytes."""
+    for t, n in ((x, "x"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (rs, "rs"),
+                 (h, "h")):
+        _bf16(t, n)
+    b, H = x.shape
+    I = w_gate.shape[0]
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moetail_shared_expert(_ptr(x), b, H, _ptr(w_gate), _ptr(w_up), I, _ptr(w_down),
+                                     _ptr(h), _ptr(rs), ws, wsb, _stream(stream))
+    _check(st, "moetail_shared_expert")
+
+
+def new_workspace(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0, device="cuda"):
+    """A device byte tensor sized for one call of `op` (None when none is needed)."""
+    n = workspace_bytes(op, b, dim0, dim1, dim2)
+    if n == 0:
+        return None
+    # the caching allocator hands out blocks aligned to at least 512 bytes
+    return torch.empty(n, dtype=torch.uint8, device=device)

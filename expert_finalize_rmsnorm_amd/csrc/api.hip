@@ -1,0 +1,190 @@
+// api.hip -- the C ABI of libmoetail (declared in include/moetail.h).
+//
+// b == 0 returns at once, before any other check ([tail] BoundTail.run
+// returns for zero rows before it checks the arguments).  Otherwise every
+// entry point checks all of its arguments first and enqueues nothing when
+// one is refused ([tail] _check_tail_args refuses a call before anything
+// launches).
+#include "moetail.h"
+
+#include <stdlib.h>
+
+#include "kernels.h"
+
+namespace {
+
+using namespace moetail;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+bool a16(const void* p) { return p != nullptr && aligned(p, 16); }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_norm_args(const void* w, int w_dtype, const uint16_t* gamma, float eps, int K, int P,
+                    int tp, int b) {
+  if (b < 0 || K <= 0 || P <= 0 || tp <= 0) return MOETAIL_EINVAL;
+  if (w_dtype != MOETAIL_F32 && w_dtype != MOETAIL_BF16) return MOETAIL_EINVAL;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;  // rejects NaN too
+  if (w == nullptr || !aligned(w, w_dtype == MOETAIL_F32 ? 4 : 2)) return MOETAIL_EINVAL;
+  if (!a16(gamma)) return MOETAIL_EINVAL;
+  if (P % 8 || P > MOETAIL_MAX_WIDTH || K > MOETAIL_MAX_ROUTES || tp > MOETAIL_MAX_TP ||
+      b > MOETAIL_MAX_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
+  return MOETAIL_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOETAIL_OK : MOETAIL_EHIP; }
+
+// Optional override of the K-split count of the projections (tuning runs).
+ProjPlan tuned(ProjPlan p, int K) {
+  const char* env = getenv("MOETAIL_PROJ_SPLITS");
+  if (env == nullptr) return p;
+  int s = atoi(env);
+  if (s < 1) return p;
+  int kps = (K + s - 1) / s;
+  kps = (kps + 31) / 32 * 32;
+  return ProjPlan{(K + kps - 1) / kps, kps};
+}
+
+struct UpprojLayout {
+  ProjPlan plan;
+  size_t y_bytes, part_bytes;
+};
+UpprojLayout upproj_layout(int b, int L, int N) {
+  UpprojLayout l;
+  l.plan = tuned(plan_upproj(b, N, L), L);
+  l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
+  l.part_bytes = round_up(proj_partial_bytes(l.plan, b, N), 256);
+  return l;
+}
+
+struct SharedLayout {
+  ProjPlan gate_up, down;
+  size_t h_bytes, part_bytes;
+};
+SharedLayout shared_layout(int b, int H, int I) {
+  SharedLayout l;
+  l.gate_up = tuned(plan_gate_up(b, I, H), H);
+  l.down = tuned(plan_down(b, H, I), I);
+  l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
+  const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I);
+  const size_t d = proj_partial_bytes(l.down, b, H);
+  l.part_bytes = round_up(g > d ? g : d, 256);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank, const int32_t* permuted_idx,
+                     const void* route_w, int route_w_dtype, const uint16_t* gamma,
+                     float gain_center, float eps, int weight_before_norm, int b, int K, int P,
+                     int tp, uint16_t* partials, uint16_t* out, hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b);
+  if (st) return st;
+  if (!a16(rows) || rows_per_rank <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4))
+    return MOETAIL_EINVAL;
+  if (partials == nullptr && out == nullptr) return MOETAIL_EINVAL;
+  if ((partials && !a16(partials)) || (out && !a16(out))) return MOETAIL_EINVAL;
+  if (!__builtin_isfinite(gain_center)) return MOETAIL_EINVAL;
+  // Without partials the combine must happen in one block (tp partials in LDS).
+  if (partials == nullptr && (tp > 8 || (size_t)tp * P * sizeof(uint16_t) > 64 * 1024))
+    return MOETAIL_EUNSUPPORTED;
+  EpArgs a{rows, rows_per_rank, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
+           gain_center, eps, weight_before_norm != 0, b, K, P, tp, partials, out};
+  return hip_status(launch_ep_finalize(a, stream));
+}
+
+int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32_t* permuted_idx,
+                        const void* route_w, int route_w_dtype, const uint16_t* gamma,
+                        float gain_center, float eps, int weight_before_norm, int b, int K, int P,
+                        int tp, uint16_t* out, hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b);
+  if (st) return st;
+  if (!a16(kpartials) || num_rows <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4) ||
+      !a16(out) || !__builtin_isfinite(gain_center))
+    return MOETAIL_EINVAL;
+  TpArgs a{kpartials, num_rows, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
+           gain_center, eps, weight_before_norm != 0, b, K, P, tp, out};
+  return hip_status(launch_tp_finalize(a, stream));
+}
+
+int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
+                                float eps, const uint16_t* w_up, int N, const uint16_t* rs, int b,
+                                int L, uint16_t* normed, uint16_t* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  if (b < 0 || tp <= 0 || N <= 0 || L <= 0) return MOETAIL_EINVAL;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
+  if (!a16(latent_partials) || !a16(gamma) || !a16(w_up) || !a16(out)) return MOETAIL_EINVAL;
+  if ((rs && !a16(rs)) || (normed && !a16(normed))) return MOETAIL_EINVAL;
+  if (L % 32 || L > MOETAIL_MAX_WIDTH || N % 64 || tp > MOETAIL_MAX_TP ||
+      b > MOETAIL_MAX_GEMM_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
+  const UpprojLayout lay = upproj_layout(b, L, N);
+  const size_t need = (normed ? 0 : lay.y_bytes) + lay.part_bytes;
+  if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+    return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* y = normed ? normed : reinterpret_cast<uint16_t*>(ws);
+  float* part = lay.part_bytes ? reinterpret_cast<float*>(ws + (normed ? 0 : lay.y_bytes)) : nullptr;
+  hipError_t e = launch_latent_norm(latent_partials, tp, b, L, gamma, eps, y, stream);
+  if (e == hipSuccess) e = launch_linear(w_up, N, L, y, b, rs, out, lay.plan, part, stream);
+  return hip_status(e);
+}
+
+int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gate,
+                          const uint16_t* w_upw, int I, const uint16_t* w_down, uint16_t* h,
+                          uint16_t* rs, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  if (b < 0 || H <= 0 || I <= 0) return MOETAIL_EINVAL;
+  if (!a16(x) || !a16(w_gate) || !a16(w_upw) || !a16(w_down) || !a16(rs)) return MOETAIL_EINVAL;
+  if (h && !a16(h)) return MOETAIL_EINVAL;
+  if (H % 64 || I % 64 || b > MOETAIL_MAX_GEMM_TOKENS) return MOETAIL_EUNSUPPORTED;
+  const SharedLayout lay = shared_layout(b, H, I);
+  const size_t need = (h ? 0 : lay.h_bytes) + lay.part_bytes;
+  if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+    return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hb = h ? h : reinterpret_cast<uint16_t*>(ws);
+  float* part = lay.part_bytes ? reinterpret_cast<float*>(ws + (h ? 0 : lay.h_bytes)) : nullptr;
+  hipError_t e = launch_gate_up(w_gate, w_upw, I, H, x, b, hb, lay.gate_up, part, stream);
+  if (e == hipSuccess) e = launch_linear(w_down, H, I, hb, b, nullptr, rs, lay.down, part, stream);
+  return hip_status(e);
+}
+
+size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
+  if (b <= 0 || b > MOETAIL_MAX_GEMM_TOKENS) return 0;
+  switch (op) {
+    case MOETAIL_OP_COMBINE_NORM_UPPROJ: {
+      if (dim0 <= 0 || dim1 <= 0 || dim0 % 32 || dim1 % 64 || dim0 > MOETAIL_MAX_WIDTH) return 0;
+      (void)dim2;
+      const UpprojLayout l = upproj_layout(b, dim0, dim1);
+      return l.y_bytes + l.part_bytes;
+    }
+    case MOETAIL_OP_SHARED_EXPERT: {
+      if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64) return 0;
+      const SharedLayout l = shared_layout(b, dim0, dim1);
+      return l.h_bytes + l.part_bytes;
+    }
+    default:
+      return 0;
+  }
+}
+
+const char* moetail_status_string(int status) {
+  switch (status) {
+    case MOETAIL_OK: return "ok";
+    case MOETAIL_EINVAL: return "invalid argument (null pointer, shape, dtype or alignment)";
+    case MOETAIL_EUNSUPPORTED: return "unsupported size (outside the library's limits)";
+    case MOETAIL_EWORKSPACE: return "workspace missing or too small";
+    case MOETAIL_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+/*
+ * moetail.h -- C ABI of libmoetail, the MoE decode tail on one MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [tail]         vllm.models.muse_spark.nvidia.specialized_decode.cutedsl.moe.tail
+ *   [tail_runtime] vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.moe.tail_runtime
+ *   [shared]       vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.moe.shared
+ *
+ * Conventions for every entry point:
+ *   - BF16 arrays are uint16_t bit patterns.  Every array pointer is a DEVICE
+ *     pointer to dense row-major memory owned by the caller; the library
+ *     keeps no pointer after the call returns and allocates nothing
+ *     ([tail] BoundTail: "run is graph-capturable and allocates nothing").
+ *     Scratch, where an entry point needs any, is the caller's workspace,
+ *     sized by moetail_workspace_bytes.
+ *   - BF16/FP32 array pointers must be 16-byte aligned (the kernels move
+ *     8 BF16 columns per 16-byte access); index and route-weight arrays
+ *     4-byte (FP32) or 2-byte (BF16) aligned; the workspace 256-byte aligned.
+ *   - Every call validates all of its arguments before it enqueues anything
+ *     ([tail] _check_tail_args: a refused call launches nothing).  A refused
+ *     call returns a negative status and leaves every buffer untouched.
+ *   - b == 0 returns MOETAIL_OK at once, before any other check, and
+ *     enqueues nothing ([tail] BoundTail.run returns for zero rows first).
+ *   - Work is enqueued asynchronously on `stream` (NULL = the default
+ *     stream); nothing synchronizes with the host, so the calls can be
+ *     captured into a HIP graph.  Results are deterministic: the same inputs
+ *     give the same bits on every call.
+ *   - Every BF16 word the library writes is rounded to nearest even from
+ *     FP32, and a -0 result is written as +0 ([tail] _TpTailKernel: "-0.0 as
+ *     +0.0"; [shared] SharedBase.push: "-0 made +0").
+ */
+#ifndef MOETAIL_H
+#define MOETAIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOETAIL_OK 0
+#define MOETAIL_EINVAL (-1)       /* null pointer, bad shape, dtype or alignment */
+#define MOETAIL_EUNSUPPORTED (-2) /* outside the library's limits below */
+#define MOETAIL_EWORKSPACE (-3)   /* workspace missing or too small */
+#define MOETAIL_EHIP (-4)         /* a HIP launch failed */
+
+/* Route-weight dtypes ([tail] _check_tail_args: BF16 or FP32). */
+#define MOETAIL_F32 0
+#define MOETAIL_BF16 1
+
+/* Operation ids for moetail_workspace_bytes. */
+#define MOETAIL_OP_FINALIZE 0
+#define MOETAIL_OP_TP_FINALIZE 1
+#define MOETAIL_OP_COMBINE_NORM_UPPROJ 2
+#define MOETAIL_OP_SHARED_EXPERT 3
+
+/* Limits.  P (and L) % 8 == 0 ([tail] 8-column fragments). */
+#define MOETAIL_MAX_WIDTH 8192  /* P, L: rows held in registers, 512 columns per wave */
+#define MOETAIL_MAX_TP 32       /* [tail] _TailReduceKernel: tp between 1 and 32 */
+#define MOETAIL_MAX_ROUTES 32   /* K */
+#define MOETAIL_MAX_TOKENS 65535
+#define MOETAIL_MAX_GEMM_TOKENS 128 /* b of the two projections */
+
+/*
+ * EP finalize ([tail] module docstring, "With expert parallelism ..."):
+ * for every simulated rank d and token t, over the routes k local to d in
+ * ascending order, with x the route's row and w its weight,
+ *     g       = fp32(gamma) + gain_center
+ *     s       = x * g  (weight_before_norm)   or   x
+ *     inv     = 1 / sqrt(sum_of_squares(s) * fp32(1/P) + eps)
+ *     n       = s * inv  (weight_before_norm) or   (x * inv) * g
+ *     partial = bf16(sum_k n * w)              FP32 from +0.0
+ * and, when `out` is given, the rank combine ([tail] _TailReduceKernel)
+ *     out[t]  = bf16(sum_{d=0}^{tp-1} fp32(partial[d][t]))   FP32 from +0.0.
+ *
+ *   rows          [tp][rows_per_rank][P] BF16: rank d's GEMM2 output rows.
+ *   permuted_idx  [tp][b][K] int32: row of route k of token t in rank d's
+ *                 rows; a value outside [0, rows_per_rank) means the route
+ *                 is not local to rank d (it contributes nothing there).
+ *   route_w       [b][K] FP32 or BF16 (route_w_dtype): full top-K weights.
+ *   gamma         [P] BF16 norm weight (ones when the norm has none).
+ *   partials      [tp][b][P] BF16 written (the resident rank-partial
+ *                 buffer), or NULL when only `out` is wanted.
+ *   out           [b][P] BF16 written, or NULL for partials only.
+ *   At least one of partials / out must be given.  partials may be NULL only
+ *   when one block can combine the token's tp partials itself (tp <= 8 and
+ *   tp * P * 2 <= 65536 bytes); otherwise MOETAIL_EUNSUPPORTED.
+ *   eps >= 0 and finite; gain_center finite.
+ *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0,
+ *   b <= 65535, rows_per_rank >= 1.
+ */
+int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank,
+                     const int32_t* permuted_idx, const void* route_w,
+                     int route_w_dtype, const uint16_t* gamma,
+                     float gain_center, float eps, int weight_before_norm,
+                     int b, int K, int P, int tp, uint16_t* partials,
+                     uint16_t* out, hipStream_t stream);
+
+/*
+ * Expert-TP finalize ([tail] module docstring, "Under expert TP ...", and
+ * _TpTailKernel): every rank holds a K-partial of every route row.
+ *     x_r    = bf16(sum_{d=0}^{tp-1} fp32(kpartials[d][idx[t][k]]))  FP32 from +0.0
+ *     out[t] = bf16(sum_k fp32(n(x_r) * w[t][k]))   routes in order, from +0.0
+ * with n() the normalization of moetail_finalize (same gain, eps, switch).
+ *
+ *   kpartials     [tp][num_rows][P] BF16.
+ *   permuted_idx  [b][K] int32 (the same on every rank); a value outside
+ *                 [0, num_rows) marks an absent route (contributes nothing).
+ *   route_w       [b][K] FP32 or BF16.   gamma [P] BF16.   out [b][P] BF16.
+ *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0.
+ */
+int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,
+                        const int32_t* permuted_idx, const void* route_w,
+                        int route_w_dtype, const uint16_t* gamma,
+                        float gain_center, float eps, int weight_before_norm,
+                        int b, int K, int P, int tp, uint16_t* out,
+                        hipStream_t stream);
+
+/*
+ * Latent combine + RMSNorm + up projection ([tail_runtime] module docstring:
+ * the latent partials are all-reduced and RMS-normalized, then the K-split
+ * up projection; MoeTailWeights: shard [7168/TP, 3584] and RMS weight):
+ *     l[t]      = bf16(sum_{d=0}^{tp-1} fp32(latent_partials[d][t]))  FP32 from +0.0
+ *     y[t]      = bf16((l * inv) * fp32(gamma)),  inv = 1/sqrt(ss(l)*fp32(1/L) + eps)
+ *     out[t][n] = bf16(sum_k fp32(w_up[n][k]) * fp32(y[t][k]) + fp32(rs[t][n]))
+ * (FP32 accumulation on the matrix cores; the rs add is skipped when rs is NULL).
+ *
+ *   latent_partials [tp][b][L] BF16.   gamma [L] BF16.
+ *   w_up            [N][L] BF16 (row n makes output column n).
+ *   rs              [b][N] BF16 shared-expert reduce-scatter partial, or NULL.
+ *   normed          [b][L] BF16 written (y), or NULL.
+ *   out             [b][N] BF16 written.
+ *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_COMBINE_NORM_UPPROJ,
+ *                   b, L, N, tp) bytes of device memory, 256-byte aligned.
+ *   Limits: b <= 128, 1 <= tp <= 32, 32 <= L <= 8192, L % 32 == 0,
+ *   N % 64 == 0.
+ */
+int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp,
+                                const uint16_t* gamma, float eps,
+                                const uint16_t* w_up, int N,
+                                const uint16_t* rs, int b, int L,
+                                uint16_t* normed, uint16_t* out,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Shared expert ([shared] module docstring and SharedUmma.owned_h / push):
+ *     gs = bf16(w_gate . x),  us = bf16(w_upw . x)        FP32 accumulation
+ *     h  = bf16(silu(fp32 gs) * fp32 us),  silu(z) = z / (1 + e^-z)
+ *     rs = bf16(w_down . h)                               FP32 accumulation
+ * (the pages name the activation but never define it; this library takes
+ * SiLU).
+ *
+ *   x       [b][H] BF16.   w_gate, w_upw [I][H] BF16 each (a stacked [2I][H]
+ *           tensor passes p and p + I*H).   w_down [H][I] BF16.
+ *   h       [b][I] BF16 written, or NULL.
+ *   rs      [b][H] BF16 written (the input of moetail_combine_norm_upproj).
+ *   workspace at least moetail_workspace_bytes(MOETAIL_OP_SHARED_EXPERT,
+ *           b, H, I, 0) bytes, 256-byte aligned.
+ *   Limits: b <= 128, H % 64 == 0, I % 64 == 0, H, I >= 64.
+ */
+int moetail_shared_expert(const uint16_t* x, int b, int H,
+                          const uint16_t* w_gate, const uint16_t* w_upw, int I,
+                          const uint16_t* w_down, uint16_t* h, uint16_t* rs,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * Workspace bytes an operation needs (0 when none):
+ *   MOETAIL_OP_FINALIZE, MOETAIL_OP_TP_FINALIZE:  0
+ *   MOETAIL_OP_COMBINE_NORM_UPPROJ: dim0 = L, dim1 = N, dim2 = tp
+ *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
+ * Returns 0 for an unknown op or out-of-range sizes.
+ */
+size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);
+
+/* A static, human-readable text for a status code. */
+const char* moetail_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,392 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every test here runs on an MI355X.  Inputs are the seeded synthetic
+workloads of ``workloads.py``; expected values come from ``oracle/`` on the
+same inputs.  Finalize and combine outputs must be within 1 BF16 step of
+the oracle and at least 99.9% bit-exact; projection outputs within
+2e-2 + 1e-2 |ref|.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import expert_finalize_rmsnorm_amd as mt
+import oracle
+import workloads
+from tests.gpu_util import (ORACLE_THREADS, SENTINEL, dev, empty_bf16, finalize_bar, gemm_bar,
+                            host)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NT = ORACLE_THREADS
+
+
+def bits(values):
+    return oracle.bf16_round(np.asarray(values, np.float32))
+
+
+# ------------------------------------------------------------ EP finalize --
+
+def run_ep(inp, wbn, wkey="w32", mode="both", **kw):
+    tp, b, P = inp["tp"], inp["b"], inp["P"]
+    rows, idx, w, gamma = dev(inp["rows"]), dev(inp["idx"]), dev(inp[wkey]), dev(inp["gamma"])
+    partials = empty_bf16(tp, b, P) if mode in ("both", "partials") else None
+    out = empty_bf16(b, P) if mode in ("both", "out") else None
+    mt.moetail_finalize(rows, idx, w, gamma, inp["gain_center"], inp["eps"], wbn,
+                        partials=partials, out=out, **kw)
+    return (host(partials) if partials is not None else None,
+            host(out) if out is not None else None)
+
+
+def oracle_ep(inp, wbn, wkey="w32"):
+    return oracle.finalize(inp["rows"], inp["idx"], inp[wkey], inp["gamma"], inp["gain_center"],
+                           inp["eps"], wbn, nthreads=NT)
+
+
+@pytest.mark.parametrize("wbn", [True, False])
+@pytest.mark.parametrize("wkey", ["w32", "w16"])
+def test_ep_tiny(wbn, wkey):
+    inp = workloads.tiny_ep_finalize(0)
+    want_p, want_o = oracle_ep(inp, wbn, wkey)
+    got_p, got_o = run_ep(inp, wbn, wkey)
+    assert np.array_equal(got_p, want_p)
+    assert np.array_equal(got_o, want_o)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("wbn", [True, False])
+@pytest.mark.parametrize("wkey", ["w32", "w16"])
+def test_ep_decode_scale(seed, wbn, wkey):
+    """b=64, top-16 over tp=8 ranks (2 local routes each), P=3584, outlier rows."""
+    inp = workloads.ep_finalize(seed)
+    want_p, want_o = oracle_ep(inp, wbn, wkey)
+    got_p, got_o = run_ep(inp, wbn, wkey, "both")
+    finalize_bar(got_p, want_p, "partials")
+    finalize_bar(got_o, want_o, "out")
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+    # out only (combine fused, partials never written) and partials only
+    _, only_o = run_ep(inp, wbn, wkey, "out")
+    only_p, _ = run_ep(inp, wbn, wkey, "partials")
+    assert np.array_equal(only_o, got_o) and np.array_equal(only_p, got_p)
+
+
+@pytest.mark.parametrize("b,K,P,tp", [(5, 3, 520, 3), (3, 7, 8, 1), (2, 32, 8192, 4),
+                                      (9, 16, 1032, 12), (1, 1, 3584, 8), (4, 4, 512, 2),
+                                      (17, 8, 7168, 8), (3, 32, 64, 32)])
+@pytest.mark.parametrize("wbn", [True, False])
+def test_ep_ragged_and_edges(b, K, P, tp, wbn):
+    per = max(1, K // tp)
+    if K % tp == 0:
+        inp = workloads.ep_finalize(b * 7 + K, b=b, K=K, P=P, tp=tp, outlier_frac=0.05)
+    else:
+        # routes spread unevenly: rank d holds the routes with k % tp == d
+        inp = workloads.ep_finalize(b, b=b, K=K, P=P, tp=1, outlier_frac=0.0)
+        rows1 = inp["rows"][0]
+        idx = np.full((tp, b, K), -1, np.int32)
+        for k in range(K):
+            idx[k % tp, :, k] = inp["idx"][0, :, k]
+        inp.update(rows=np.ascontiguousarray(np.broadcast_to(rows1, (tp,) + rows1.shape)),
+                   idx=idx, tp=tp)
+    del per
+    want_p, want_o = oracle_ep(inp, wbn)
+    got_p, got_o = run_ep(inp, wbn)
+    finalize_bar(got_p, want_p, "partials")
+    finalize_bar(got_o, want_o, "out")
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+
+
+def test_ep_absent_and_out_of_range_indices():
+    inp = workloads.ep_finalize(5, b=6, K=8, P=1024, tp=4)
+    idx = inp["idx"].copy()
+    idx[idx < 0] = np.where(np.arange((idx < 0).sum()) % 2 == 0, -7, inp["R"] + 3)
+    inp["idx"] = idx
+    want_p, want_o = oracle_ep(inp, True)
+    got_p, got_o = run_ep(inp, True)
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)["case"]
+
+
+def test_ep_golden_rank_and_route_order_and_negzero():
+    case = _golden("rank_order.json")
+    tp, P = case["tp"], case["P"]
+    idx = np.full((tp, 1, tp), -1, np.int32)
+    for d in range(tp):
+        idx[d, 0, d] = 0
+    inp = dict(rows=bits(np.ones((tp, 1, P))), idx=idx, w32=np.array([case["w"]], np.float32),
+               gamma=np.zeros(P, np.uint16), gain_center=case["gain_center"], eps=case["eps"],
+               tp=tp, b=1, P=P)
+    got_p, got_o = run_ep(inp, True)
+    assert [f"{int(v):04x}" for v in got_p[:, 0, 0]] == case["expected_partials_hex"]
+    assert all(f"{int(v):04x}" == case["expected_out_hex"] for v in got_o.ravel())
+
+    case = _golden("route_order.json")
+    K, P = case["K"], case["P"]
+    inp = dict(rows=bits(np.ones((1, K, P))), idx=np.arange(K, dtype=np.int32).reshape(1, 1, K),
+               w32=np.array([case["w"]], np.float32), gamma=np.zeros(P, np.uint16),
+               gain_center=case["gain_center"], eps=case["eps"], tp=1, b=1, P=P)
+    for wbn in (True, False):
+        _, got_o = run_ep(inp, wbn)
+        assert all(f"{int(v):04x}" == case["expected_out_hex"] for v in got_o.ravel())
+
+    case = _golden("negzero.json")
+    P = case["P"]
+    inp = dict(rows=bits(np.array(case["row"])).reshape(1, 1, P),
+               idx=np.zeros((1, 1, 1), np.int32),
+               w32=np.array([[case["w_sign"] * 2.0 ** case["w_log2"]]], np.float32),
+               gamma=np.zeros(P, np.uint16), gain_center=case["gain_center"], eps=case["eps"],
+               tp=1, b=1, P=P)
+    got_p, got_o = run_ep(inp, case["weight_before_norm"])
+    assert [f"{int(v):04x}" for v in got_o.ravel()] == case["expected_out_hex"]
+    assert [f"{int(v):04x}" for v in got_p.ravel()] == case["expected_out_hex"]
+
+
+def test_ep_b0_and_refused_calls_write_nothing():
+    inp = workloads.ep_finalize(0, b=4, K=16, P=3584, tp=8)
+    rows, idx, w, gamma = dev(inp["rows"]), dev(inp["idx"]), dev(inp["w32"]), dev(inp["gamma"])
+    out = empty_bf16(4, 3584)
+    mt.moetail_finalize(rows, idx[:, :0], w[:0], gamma, 1.0, 1e-6, True, out=out[:0])
+    with pytest.raises(mt.MoetailError):
+        mt.moetail_finalize(rows, idx, w, gamma, 1.0, -1.0, True, out=out)  # eps < 0
+    assert np.all(host(out) == SENTINEL)
+
+
+def test_ep_repeatable_and_graph_replay():
+    inp = workloads.ep_finalize(3)
+    rows, idx, w, gamma = dev(inp["rows"]), dev(inp["idx"]), dev(inp["w32"]), dev(inp["gamma"])
+    out = empty_bf16(64, 3584)
+    partials = empty_bf16(8, 64, 3584)
+    first = None
+    for _ in range(5):
+        mt.moetail_finalize(rows, idx, w, gamma, 1.0, 1e-6, True, partials=partials, out=out)
+        cur = (host(partials), host(out))
+        if first is None:
+            first = cur
+        assert np.array_equal(cur[0], first[0]) and np.array_equal(cur[1], first[1])
+    out.fill_(SENTINEL)
+    partials.fill_(SENTINEL)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mt.moetail_finalize(rows, idx, w, gamma, 1.0, 1e-6, True, partials=partials, out=out)
+    for _ in range(3):
+        out.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), first[1]) and np.array_equal(host(partials), first[0])
+
+
+# ------------------------------------------------------------- expert TP --
+
+def run_tp(inp, wbn, wkey="w32"):
+    out = empty_bf16(inp["b"], inp["P"])
+    mt.moetail_tp_finalize(dev(inp["kpart"]), dev(inp["idx"]), dev(inp[wkey]), dev(inp["gamma"]),
+                           inp["gain_center"], inp["eps"], wbn, out)
+    return host(out)
+
+
+@pytest.mark.parametrize("wbn,wkey", [(False, "w32"), (False, "w16"), (True, "w32")])
+def test_tp_full_scale(wbn, wkey):
+    """b=128, K=16, P=7168, tp=8 K-partials of every route row (235 MB)."""
+    inp = workloads.tp_finalize(0)
+    want = oracle.tp_finalize(inp["kpart"], inp["idx"], inp[wkey], inp["gamma"],
+                              inp["gain_center"], inp["eps"], wbn, nthreads=NT)
+    got = run_tp(inp, wbn, wkey)
+    finalize_bar(got, want, "tp out")
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("b,K,P,tp", [(7, 5, 1032, 3), (3, 20, 520, 2), (2, 16, 8192, 1),
+                                      (5, 1, 8, 32), (4, 32, 3584, 4)])
+@pytest.mark.parametrize("wbn", [True, False])
+def test_tp_ragged_and_edges(b, K, P, tp, wbn):
+    inp = workloads.tp_finalize(b + K, b=b, K=K, P=P, tp=tp, num_rows=b * K + 3)
+    idx = inp["idx"].copy()
+    idx[0, K // 2] = -1                 # absent route
+    idx[b - 1, K - 1] = inp["num_rows"] + 9  # past the end: absent too
+    inp["idx"] = idx
+    inp["gain_center"] = 0.5
+    want = oracle.tp_finalize(inp["kpart"], idx, inp["w32"], inp["gamma"], 0.5, inp["eps"], wbn,
+                              nthreads=NT)
+    got = run_tp(inp, wbn)
+    finalize_bar(got, want, "tp out")
+    assert np.array_equal(got, want)
+
+
+def test_tp_golden_round_before_norm():
+    case = _golden("tp_round_before_norm.json")
+    P = case["P"]
+    kpart = np.zeros((2, 1, P), np.uint16)
+    kpart[0, 0] = bits(np.ones(P))
+    kpart[1, 0, 0] = bits([2.0 ** -8])[0]
+    inp = dict(kpart=kpart, idx=np.array(case["idx"], np.int32),
+               w32=np.array([case["w"]], np.float32), gamma=np.zeros(P, np.uint16),
+               gain_center=case["gain_center"], eps=case["eps"], b=1, P=P)
+    got = run_tp(inp, True)
+    assert [f"{int(v):04x}" for v in got.ravel()] == case["expected_out_hex"]
+
+
+# ------------------------------------ latent combine + norm + up projection --
+
+def run_upproj(inp, rs=None, with_normed=True):
+    b, L, N, tp = inp["b"], inp["L"], inp["N"], inp["tp"]
+    out = empty_bf16(b, N)
+    normed = empty_bf16(b, L) if with_normed else None
+    ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L, N, tp)
+    mt.moetail_combine_norm_upproj(dev(inp["lat"]), dev(inp["gamma"]), inp["eps"],
+                                   dev(inp["w_up"]), out, rs=None if rs is None else dev(rs),
+                                   normed=normed, workspace=ws)
+    return (host(normed) if normed is not None else None), host(out)
+
+
+@pytest.mark.parametrize("b", [1, 8, 32, 64])
+def test_upproj_scale(b):
+    """tp=8 latent partials [8,b,3584] -> RMSNorm -> W_up [7168,3584]."""
+    inp = workloads.upproj(0, b=b)
+    want_n, want_o = oracle.combine_norm_upproj(inp["lat"], inp["gamma"], inp["eps"],
+                                                inp["w_up"], nthreads=NT)
+    got_n, got_o = run_upproj(inp)
+    assert np.array_equal(got_n, want_n)
+    gemm_bar(got_o, want_o, f"upproj b={b}")
+    _, got_o2 = run_upproj(inp, with_normed=False)  # y kept in the workspace
+    assert np.array_equal(got_o2, got_o)
+
+
+def test_upproj_with_reduce_scatter_partial():
+    inp = workloads.upproj(1, b=64, with_rs=True)
+    want_n, want_o = oracle.combine_norm_upproj(inp["lat"], inp["gamma"], inp["eps"],
+                                                inp["w_up"], inp["rs"], nthreads=NT)
+    got_n, got_o = run_upproj(inp, rs=inp["rs"])
+    assert np.array_equal(got_n, want_n)
+    gemm_bar(got_o, want_o, "upproj + rs")
+
+
+@pytest.mark.parametrize("b,tp,L,N", [(5, 3, 544, 128), (17, 1, 32, 64), (128, 2, 1024, 256),
+                                      (3, 32, 8192, 64)])
+def test_upproj_ragged(b, tp, L, N):
+    inp = workloads.upproj(b + L, b=b, tp=tp, L=L, N=N, with_rs=True)
+    want_n, want_o = oracle.combine_norm_upproj(inp["lat"], inp["gamma"], inp["eps"],
+                                                inp["w_up"], inp["rs"], nthreads=NT)
+    got_n, got_o = run_upproj(inp, rs=inp["rs"])
+    assert np.array_equal(got_n, want_n)
+    gemm_bar(got_o, want_o, "upproj ragged")
+
+
+def test_upproj_unit_rows_and_zero_weights():
+    inp = workloads.upproj(2, b=33, tp=4, L=1024, N=192)
+    perm = np.random.default_rng(0).integers(0, 1024, 192)
+    w = np.zeros((192, 1024), np.float32)
+    w[np.arange(192), perm] = 1.0
+    inp["w_up"] = bits(w)
+    got_n, got_o = run_upproj(inp)
+    assert np.array_equal(got_o, got_n[:, perm])  # one exact product per output
+    rs = bits(np.random.default_rng(1).standard_normal((33, 192)))
+    rs[0, :4] = 0x8000
+    inp["w_up"] = np.zeros((192, 1024), np.uint16)
+    _, got_o = run_upproj(inp, rs=rs)
+    want = rs.copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(got_o, want)
+
+
+# ----------------------------------------------------------- shared expert --
+
+def run_shared(inp, with_h=True):
+    b, H, I = inp["b"], inp["H"], inp["I"]
+    rs = empty_bf16(b, H)
+    h = empty_bf16(b, I) if with_h else None
+    ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
+    mt.moetail_shared_expert(dev(inp["x"]), dev(inp["w_gate"]), dev(inp["w_up"]),
+                             dev(inp["w_down"]), rs, h=h, workspace=ws)
+    return (host(h) if h is not None else None), host(rs)
+
+
+def sample_tokens(b):
+    return sorted({0, 1, min(15, b - 1), min(16, b - 1), b // 2, b - 1})
+
+
+@pytest.mark.parametrize("b", [16, 32, 64, 128])
+def test_shared_scale(b):
+    """x [b,7168], W_gate/W_up [6144,7168], W_down [7168,6144]; the oracle
+    runs on a sample of the tokens (tokens are independent)."""
+    inp = workloads.shared(0, b=b)
+    got_h, got_rs = run_shared(inp)
+    sel = sample_tokens(b)
+    want_h, want_rs = oracle.shared_expert(inp["x"][sel], inp["w_gate"], inp["w_up"],
+                                           inp["w_down"], nthreads=NT)
+    gemm_bar(got_h[sel], want_h, f"h b={b}")
+    gemm_bar(got_rs[sel], want_rs, f"rs b={b}")
+    _, got_rs2 = run_shared(inp, with_h=False)  # h kept in the workspace
+    assert np.array_equal(got_rs2, got_rs)
+
+
+@pytest.mark.parametrize("b,H,I", [(5, 512, 256), (33, 256, 128), (1, 64, 64), (128, 128, 192)])
+def test_shared_small_full(b, H, I):
+    inp = workloads.shared(b + H, b=b, H=H, I=I)
+    want_h, want_rs = oracle.shared_expert(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                                           nthreads=NT)
+    got_h, got_rs = run_shared(inp)
+    gemm_bar(got_h, want_h, "h")
+    gemm_bar(got_rs, want_rs, "rs")
+
+
+def test_shared_unit_rows():
+    rng = np.random.default_rng(4)
+    b, H, I = 20, 256, 128
+    x = bits(rng.standard_normal((b, H)) * 3)
+    a, c = rng.integers(0, H, I), rng.integers(0, H, I)
+    wg = np.zeros((I, H), np.float32)
+    wu = np.zeros((I, H), np.float32)
+    wg[np.arange(I), a] = 1.0
+    wu[np.arange(I), c] = 1.0
+    sel = rng.integers(0, I, H)
+    wd = np.zeros((H, I), np.float32)
+    wd[np.arange(H), sel] = 1.0
+    inp = dict(x=x, w_gate=bits(wg), w_up=bits(wu), w_down=bits(wd), b=b, H=H, I=I)
+    got_h, got_rs = run_shared(inp)
+    want_h, _ = oracle.shared_expert(x, inp["w_gate"], inp["w_up"], inp["w_down"])
+    gemm_bar(got_h, want_h, "unit-row h")
+    assert np.array_equal(got_rs, got_h[:, sel])  # one exact product per output
+    zh, zrs = run_shared(dict(inp, x=np.zeros_like(x)))
+    assert not zh.any() and not zrs.any()
+
+
+def test_projections_graph_replay():
+    inp = workloads.upproj(4, b=32, with_rs=True)
+    sh = workloads.shared(4, b=32)
+    lat, gamma, w_up, rs_in = dev(inp["lat"]), dev(inp["gamma"]), dev(inp["w_up"]), dev(inp["rs"])
+    x, wg, wu, wd = dev(sh["x"]), dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"])
+    out, rs = empty_bf16(32, 7168), empty_bf16(32, 7168)
+    ws1 = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, 32, 3584, 7168, 8)
+    ws2 = mt.new_workspace(mt.OP_SHARED_EXPERT, 32, 7168, 6144)
+
+    def step():
+        mt.moetail_shared_expert(x, wg, wu, wd, rs, workspace=ws2)
+        mt.moetail_combine_norm_upproj(lat, gamma, 1e-6, w_up, out, rs=rs, workspace=ws1)
+
+    step()
+    eager = (host(rs), host(out))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for _ in range(3):
+        out.fill_(SENTINEL)
+        rs.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(rs), eager[0]) and np.array_equal(host(out), eager[1])
+    del rs_in

@@ -50,7 +50,7 @@ def lib() -> ctypes.CDLL:
         L.moetail_finalize.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, I32, I32, I32,
                                        P, P, P]
         L.moetail_tp_finalize.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, I32, I32, I32,
-                                          P, P]
+                                          P, P, SZ, P]
         L.moetail_combine_norm_upproj.argtypes = [P, I32, P, F, P, I32, P, I32, I32, P, P, P,
                                                   SZ, P]
         L.moetail_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, SZ, P]
@@ -126,17 +126,20 @@ def moetail_finalize(rows, permuted_idx, route_w, gamma, gain_center, eps, weigh
 
 
 def moetail_tp_finalize(kpartials, permuted_idx, route_w, gamma, gain_center, eps,
-                        weight_before_norm, out, stream=None):
-    """kpartials [tp, num_rows, P], permuted_idx [b, K], route_w [b, K]; writes out [b, P]."""
+                        weight_before_norm, out, workspace=None, stream=None):
+    """kpartials [tp, num_rows, P], permuted_idx [b, K], route_w [b, K]; writes out [b, P].
+    workspace: at least workspace_bytes(OP_TP_FINALIZE, b, K, P) bytes."""
     _bf16(kpartials, "kpartials"), _bf16(gamma, "gamma"), _bf16(out, "out")
     tp, num_rows, P = kpartials.shape
     b, K = permuted_idx.shape
     if permuted_idx.dtype != torch.int32:
         raise TypeError("permuted_idx must be int32")
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().moetail_tp_finalize(_ptr(kpartials), num_rows, _ptr(permuted_idx),
                                    _ptr(route_w), _weights(route_w), _ptr(gamma),
                                    float(gain_center), float(eps), int(bool(weight_before_norm)),
-                                   b, K, P, tp, _ptr(out), _stream(stream))
+                                   b, K, P, tp, _ptr(out), ws, wsb, _stream(stream))
     _check(st, "moetail_tp_finalize")
 
 

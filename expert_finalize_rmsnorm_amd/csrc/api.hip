@@ -7,6 +7,7 @@
 // launches).
 #include "moetail.h"
 
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "kernels.h"
@@ -35,15 +36,24 @@ int check_norm_args(const void* w, int w_dtype, const uint16_t* gamma, float eps
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOETAIL_OK : MOETAIL_EHIP; }
 
-// Optional override of the K-split count of the projections (tuning runs).
-ProjPlan tuned(ProjPlan p, int K) {
-  const char* env = getenv("MOETAIL_PROJ_SPLITS");
-  if (env == nullptr) return p;
-  int s = atoi(env);
-  if (s < 1) return p;
-  int kps = (K + s - 1) / s;
-  kps = (kps + 31) / 32 * 32;
-  return ProjPlan{(K + kps - 1) / kps, kps};
+// The library's projection plans, with optional overrides read once from
+// the environment (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES and _BLOCKS
+// for KIND in UPPROJ, GATEUP, DOWN.
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+ProjTuning tuning(const char* kind) {
+  char n1[64], n2[64], n3[64];
+  snprintf(n1, sizeof n1, "MOETAIL_%s_SPLITS", kind);
+  snprintf(n2, sizeof n2, "MOETAIL_%s_WAVES", kind);
+  snprintf(n3, sizeof n3, "MOETAIL_%s_BLOCKS", kind);
+  return ProjTuning{env_int(n1), env_int(n2), env_int(n3)};
+}
+
+// The expert-TP path keeps its rank-summed route rows [b][K][P] BF16.
+size_t tp_workspace(int b, int K, int P) {
+  return round_up(sizeof(uint16_t) * (size_t)b * K * P, 256);
 }
 
 struct UpprojLayout {
@@ -52,9 +62,9 @@ struct UpprojLayout {
 };
 UpprojLayout upproj_layout(int b, int L, int N) {
   UpprojLayout l;
-  l.plan = tuned(plan_upproj(b, N, L), L);
+  l.plan = plan_projection(b, N, L, tuning("UPPROJ"));
   l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
-  l.part_bytes = round_up(proj_partial_bytes(l.plan, b, N), 256);
+  l.part_bytes = round_up(proj_partial_bytes(l.plan, b, N, false), 256);
   return l;
 }
 
@@ -64,11 +74,11 @@ struct SharedLayout {
 };
 SharedLayout shared_layout(int b, int H, int I) {
   SharedLayout l;
-  l.gate_up = tuned(plan_gate_up(b, I, H), H);
-  l.down = tuned(plan_down(b, H, I), I);
+  l.gate_up = plan_projection(b, 2 * I, H, tuning("GATEUP"));
+  l.down = plan_projection(b, H, I, tuning("DOWN"));
   l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
-  const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I);
-  const size_t d = proj_partial_bytes(l.down, b, H);
+  const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I, true);
+  const size_t d = proj_partial_bytes(l.down, b, H, false);
   l.part_bytes = round_up(g > d ? g : d, 256);
   return l;
 }
@@ -89,9 +99,6 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
   if (partials == nullptr && out == nullptr) return MOETAIL_EINVAL;
   if ((partials && !a16(partials)) || (out && !a16(out))) return MOETAIL_EINVAL;
   if (!__builtin_isfinite(gain_center)) return MOETAIL_EINVAL;
-  // Without partials the combine must happen in one block (tp partials in LDS).
-  if (partials == nullptr && (tp > 8 || (size_t)tp * P * sizeof(uint16_t) > 64 * 1024))
-    return MOETAIL_EUNSUPPORTED;
   EpArgs a{rows, rows_per_rank, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
            gain_center, eps, weight_before_norm != 0, b, K, P, tp, partials, out};
   return hip_status(launch_ep_finalize(a, stream));
@@ -100,15 +107,20 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
 int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32_t* permuted_idx,
                         const void* route_w, int route_w_dtype, const uint16_t* gamma,
                         float gain_center, float eps, int weight_before_norm, int b, int K, int P,
-                        int tp, uint16_t* out, hipStream_t stream) {
+                        int tp, uint16_t* out, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
   int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b);
   if (st) return st;
   if (!a16(kpartials) || num_rows <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4) ||
       !a16(out) || !__builtin_isfinite(gain_center))
     return MOETAIL_EINVAL;
+  const size_t need = tp_workspace(b, K, P);
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
+    return MOETAIL_EWORKSPACE;
   TpArgs a{kpartials, num_rows, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
-           gain_center, eps, weight_before_norm != 0, b, K, P, tp, out};
+           gain_center, eps, weight_before_norm != 0, b, K, P, tp, out,
+           static_cast<uint16_t*>(workspace)};
   return hip_status(launch_tp_finalize(a, stream));
 }
 
@@ -158,6 +170,12 @@ int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gat
 }
 
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
+  if (op == MOETAIL_OP_TP_FINALIZE) {
+    if (b <= 0 || b > MOETAIL_MAX_TOKENS || dim0 <= 0 || dim0 > MOETAIL_MAX_ROUTES || dim1 <= 0 ||
+        dim1 % 8 || dim1 > MOETAIL_MAX_WIDTH)
+      return 0;
+    return tp_workspace(b, dim0, dim1);
+  }
   if (b <= 0 || b > MOETAIL_MAX_GEMM_TOKENS) return 0;
   switch (op) {
     case MOETAIL_OP_COMBINE_NORM_UPPROJ: {

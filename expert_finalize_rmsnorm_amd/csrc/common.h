@@ -60,12 +60,25 @@ __device__ __forceinline__ uint4 pack8(const float (&v)[8]) {
 
 // --------------------------------------------------------- reductions ---
 
-// Wave-wide sum by xor butterfly: after the step with offset o every lane
-// of an aligned group of 2o lanes holds that group's sum (a + a', and FP32
-// addition commutes, so both partners agree bit for bit).
+// Wave-wide butterfly sum.  After the step that pairs aligned groups of o
+// lanes, every lane of an aligned group of 2o lanes holds that group's sum,
+// computed as (own group) + (partner group).  Every lane of a group holds
+// the same value, so which partner lane is read does not change a bit, and
+// FP32 addition commutes, so both partners agree: the result equals the xor
+// butterfly with offsets 1, 2, 4, ..., 32.  Steps 1 and 2 use quad
+// permutes, 4 and 8 the half-row and row mirrors (DPP: no LDS round trip),
+// 16 and 32 a lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
 __device__ __forceinline__ float wave_butterfly_sum(float s) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) s = s + __shfl_xor(s, o, kWave);
+  s = s + dpp_f<0xb1>(s);   // quad_perm [1,0,3,2]: lane ^ 1
+  s = s + dpp_f<0x4e>(s);   // quad_perm [2,3,0,1]: lane ^ 2
+  s = s + dpp_f<0x141>(s);  // row_half_mirror: the other 4 of 8
+  s = s + dpp_f<0x140>(s);  // row_mirror: the other 8 of 16
+  s = s + __shfl_xor(s, 16, kWave);
+  s = s + __shfl_xor(s, 32, kWave);
   return s;
 }
 

@@ -34,14 +34,6 @@ __device__ __forceinline__ float load_weight(const void* w, int64_t i) {
   return reinterpret_cast<const float*>(w)[i];
 }
 
-// Gains of one 8-column chunk.
-__device__ __forceinline__ void load_gains(const uint16_t* gamma, int col, float gc,
-                                           float (&g)[8]) {
-  unpack8(load16(gamma + col), g);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) g[c] = g[c] + gc;
-}
-
 // Normalized, route-weighted products of one chunk, added into acc.
 template <bool WBN>
 __device__ __forceinline__ void add_products(const uint4& xq, const float (&g)[8], float inv,
@@ -75,264 +67,243 @@ __device__ __forceinline__ float chunk_ss(const uint4& xq, const float (&g)[8]) 
   return chunk_sum_of_squares(v);
 }
 
-// ------------------------------------------------------------ EP finalize -
+// ------------------------------------------------------- finalize kernel -
 //
-// One wavefront per (rank d, token t).  Lane k < K holds route k's row index
-// and weight; a ballot gives the wave-uniform mask of the rank's local
-// routes, walked in ascending order.  The row of the next local route is
-// loaded before the current one is reduced, so two rows are in flight.
-// Lane l holds columns 512 j + 8 l .. + 7 of every block j in registers.
+// One block per token t, one wave per 512-column block of the row (P <= 8192:
+// at most 16 waves); lane l of wave j owns columns 512 j + 8 l .. + 7.
 //
-// FUSE: the block is the tp waves of one token; each wave also leaves its
-// BF16 partial in LDS and, after one barrier, the block adds the tp
-// partials in rank order and writes the combined row (no second launch and
-// no re-read of the partials from memory).
-template <int NB, bool WBN, bool WBF16, bool FUSE>
-__global__ void __launch_bounds__(512) ep_finalize_kernel(EpArgs a) {
-  extern __shared__ uint4 staged[];  // FUSE: [tp][P / 8]
+//  1. Wave 0 lists the token's local (rank, route) pairs in rank order and,
+//     within a rank, in ascending route order, with their row and weight, in
+//     LDS (all index loads in flight at once, one ballot per 64 entries).
+//  2. The pairs are taken in batches of kSlots (one LDS read hands lane s
+//     pair s; the rest are lane reads): every wave loads its chunk of
+//     every row of the batch at once (one memory round trip per batch), adds
+//     its squares (the gains first with weight_before_norm) and reduces them
+//     across the wave; the block shares meet in LDS.
+//  3. After a barrier each pair's inverse RMS is the in-order sum of its
+//     block shares; the waves walk the batch's pairs in order, adding the
+//     weighted normalized products into the current rank's FP32 partial.
+//     When the walk passes the last route of a rank, that rank's partial is
+//     rounded to BF16 (-0 as +0), stored if asked, and added in rank order
+//     into the combined row; ranks without local routes give +0 partials.
+//
+// The expert-TP path runs the same kernel in "dense" mode over its rank-
+// summed rows: route k of token t reads row t*K + k of one rank, present
+// when its index lies in [0, idx_limit).
+constexpr int kMaxPairs = MOETAIL_KMAX_PAIRS;
+
+struct FinArgs {
+  const uint16_t* rows;
+  int64_t R;            // rows per rank (EP)
+  const int32_t* idx;   // EP: [tp][b][K]; dense: [b][K]
+  int64_t idx_limit;    // a route is present when 0 <= idx < idx_limit
+  int dense;
+  const void* w;        // [b][K]
+  const uint16_t* gamma;
+  float gain_center, eps;
+  int b, K, P, tp;
+  uint16_t* partials;   // [tp][b][P] or null
+  uint16_t* out;        // [b][P] or null
+};
+
+struct Pair {
+  long long row;  // row index into `rows` (units of P elements)
+  float w;
+  int rank;
+};
+
+// kSlots rows in flight per lane: 16 when the block has at most 8 waves
+// (256 VGPRs per lane), 8 for wider rows (up to 16 waves, 128 VGPRs).
+template <bool WBN, bool WBF16, int kSlots, int kMaxThreads>
+__global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
+  __shared__ Pair pairs[kMaxPairs];
+  __shared__ float block_ss[kSlots][16];
+  __shared__ int pair_count;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  int d, t;
-  if (FUSE) {
-    t = blockIdx.x;
-    d = wave;
-  } else {
-    const int pair = blockIdx.x * (blockDim.x / kWave) + wave;
-    if (pair >= a.tp * a.b) return;  // whole wave leaves together
-    d = pair / a.b;
-    t = pair - d * a.b;
-  }
-  const int P = a.P;
-
-  int my_row = -1;
-  float my_w = 0.0f;
-  if (lane < a.K) {
-    my_row = a.idx[((int64_t)d * a.b + t) * a.K + lane];
-    my_w = load_weight<WBF16>(a.w, (int64_t)t * a.K + lane);
-  }
-  const bool local = lane < a.K && my_row >= 0 && (int64_t)my_row < a.R;
-  uint64_t routes = __ballot(local);
-
-  float g[NB][8];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int col = j * kBlockCols + lane * kChunk;
-    if (col < P) load_gains(a.gamma, col, a.gain_center, g[j]);
-  }
-
-  const uint16_t* rank_rows = a.rows + (int64_t)d * a.R * P;
-  auto load_row = [&](int r, uint4 (&dst)[NB]) {
-    const uint16_t* row = rank_rows + (int64_t)r * P;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = j * kBlockCols + lane * kChunk;
-      if (col < P) dst[j] = load16(row + col);
-    }
-  };
-
-  float acc[NB][8];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[j][c] = 0.0f;
-
-  const float inv_width = (float)(1.0 / (double)P);
-  uint4 cur[NB];
-  int k = -1;
-  if (routes) {
-    k = __builtin_ctzll(routes);
-    routes &= routes - 1;
-    load_row(readlane_i(my_row, k), cur);
-  }
-  while (k >= 0) {
-    int kn = -1;
-    uint4 nxt[NB];
-    if (routes) {
-      kn = __builtin_ctzll(routes);
-      routes &= routes - 1;
-      load_row(readlane_i(my_row, kn), nxt);
-    }
-    const float wk = readlane_f(my_w, k);
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = j * kBlockCols + lane * kChunk;
-      float s = 0.0f;
-      if (col < P) s = chunk_ss<WBN>(cur[j], g[j]);
-      s = wave_butterfly_sum(s);
-      ss = ss + s;
-    }
-    const float inv = inv_rms(ss, inv_width, a.eps);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = j * kBlockCols + lane * kChunk;
-      if (col < P) add_products<WBN>(cur[j], g[j], inv, wk, acc[j]);
-    }
-    k = kn;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) cur[j] = nxt[j];
-  }
-
-  const int nchunks = P / kChunk;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int col = j * kBlockCols + lane * kChunk;
-    if (col < P) {
-      const uint4 q = pack8_pz(acc[j]);
-      if (a.partials) store16(a.partials + ((int64_t)d * a.b + t) * P + col, q);
-      if (FUSE) staged[d * nchunks + col / kChunk] = q;
-    }
-  }
-  if (FUSE) {
-    __syncthreads();
-    for (int c = threadIdx.x; c < nchunks; c += blockDim.x) {
-      float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-      for (int r = 0; r < a.tp; ++r) {
-        float v[8];
-        unpack8(staged[r * nchunks + c], v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
-      }
-      store16(a.out + (int64_t)t * P + c * kChunk, pack8_pz(s));
-    }
-  }
-}
-
-// Rank combine from memory: one thread per 8-column chunk of a token.
-__global__ void __launch_bounds__(256) rank_combine_kernel(const uint16_t* partials, int tp,
-                                                           int b, int P, uint16_t* out) {
-  const int nchunks = P / kChunk;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)b * nchunks) return;
-  const int t = (int)(i / nchunks);
-  const int c = (int)(i - (int64_t)t * nchunks);
-  float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  for (int r = 0; r < tp; ++r) {
-    float v[8];
-    unpack8(load16(partials + ((int64_t)r * b + t) * P + c * kChunk), v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
-  }
-  store16(out + (int64_t)t * P + c * kChunk, pack8_pz(s));
-}
-
-template <int NB, bool WBN, bool WBF16, bool FUSE>
-hipError_t ep_launch(const EpArgs& a, hipStream_t stream) {
-  if (FUSE) {
-    const size_t lds = (size_t)a.tp * a.P * sizeof(uint16_t);
-    hipLaunchKernelGGL((ep_finalize_kernel<NB, WBN, WBF16, true>), dim3(a.b), dim3(kWave * a.tp),
-                       lds, stream, a);
-  } else {
-    const int waves = a.tp * a.b;
-    const int per_block = 4;
-    hipLaunchKernelGGL((ep_finalize_kernel<NB, WBN, WBF16, false>),
-                       dim3((waves + per_block - 1) / per_block), dim3(kWave * per_block), 0,
-                       stream, a);
-  }
-  return hipGetLastError();
-}
-
-template <int NB>
-hipError_t ep_dispatch_nb(const EpArgs& a, bool fuse, hipStream_t s) {
-  const int key = (a.wbn ? 4 : 0) | (a.w_bf16 ? 2 : 0) | (fuse ? 1 : 0);
-  switch (key) {
-    case 0: return ep_launch<NB, false, false, false>(a, s);
-    case 1: return ep_launch<NB, false, false, true>(a, s);
-    case 2: return ep_launch<NB, false, true, false>(a, s);
-    case 3: return ep_launch<NB, false, true, true>(a, s);
-    case 4: return ep_launch<NB, true, false, false>(a, s);
-    case 5: return ep_launch<NB, true, false, true>(a, s);
-    case 6: return ep_launch<NB, true, true, false>(a, s);
-    default: return ep_launch<NB, true, true, true>(a, s);
-  }
-}
-
-// --------------------------------------------------------- expert-TP ----
-//
-// One block per token, one wave per 512-column block of the row (P <= 8192:
-// at most 16 waves).  Pass 1, routes in order: every lane sums its chunk of
-// the route's tp K-partials in rank order (FP32 from 0), rounds the sum to
-// BF16 (kept in registers) and adds its squares; the wave butterfly gives
-// the block's share, left in LDS.  After one barrier every wave folds the
-// block shares of each route in block order into inv, and pass 2 adds the
-// weighted, normalized products of the routes in order from 0.
-template <bool WBN, bool WBF16, int KMAX>
-__global__ void __launch_bounds__(1024) tp_finalize_kernel(TpArgs a) {
-  __shared__ float block_ss[KMAX][16];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nwaves = blockDim.x / kWave;
   const int t = blockIdx.x;
   const int P = a.P;
+
+  // Wave 0 lists the local (rank, route) pairs.  Entry e = d * K + k (rank
+  // major, route minor: the order of the sums); lane l holds entries l,
+  // l + 64, ...; every index load is in flight at once, and a ballot per
+  // group of 64 entries places each local pair.
   const int col = (wave * kWave + lane) * kChunk;
   const bool has = col < P;
-
-  int my_row = -1;
-  float my_w = 0.0f;
-  if (lane < a.K) {
-    my_row = a.idx[(int64_t)t * a.K + lane];
-    my_w = load_weight<WBF16>(a.w, (int64_t)t * a.K + lane);
-  }
-  float g[8];
-  if (has) load_gains(a.gamma, col, a.gain_center, g);
-
-  const int64_t rank_stride = a.num_rows * (int64_t)P;
-  uint4 xr[KMAX];
+  const int colc = has ? col : P - kChunk;  // lanes past the row read a valid chunk
+  const uint4 gq = load16(a.gamma + colc);
+  if (wave == 0) {
+    const int nent = a.dense ? a.K : a.tp * a.K;
+    const int ngroups = (nent + kWave - 1) / kWave;
+    const float wk = lane < a.K ? load_weight<WBF16>(a.w, (int64_t)t * a.K + lane) : 0.0f;
+    int rr[kMaxPairs / kWave];
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    if (k < a.K) {
-      const int r = readlane_i(my_row, k);
-      if (r >= 0 && (int64_t)r < a.num_rows) {
-        float s = 0.0f;
-        if (has) {
-          const uint16_t* src = a.kpart + (int64_t)r * P + col;
-          float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-          for (int rank = 0; rank < a.tp; ++rank) {
-            float v[8];
-            unpack8(load16(src + rank * rank_stride), v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
-          }
-          xr[k] = pack8(sum);
-          s = chunk_ss<WBN>(xr[k], g);
-        }
-        s = wave_butterfly_sum(s);
-        if (lane == 0) block_ss[k][wave] = s;
+    for (int q = 0; q < kMaxPairs / kWave; ++q) {
+      rr[q] = -1;
+      const int e = kWave * q + lane;
+      if (q < ngroups && e < nent) {
+        const int d = e / a.K, k = e - d * a.K;
+        rr[q] = a.dense ? a.idx[(int64_t)t * a.K + k] : a.idx[((int64_t)d * a.b + t) * a.K + k];
       }
     }
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxPairs / kWave; ++q) {
+      if (q < ngroups) {
+        const int e = min(kWave * q + lane, nent - 1);
+        const int d = e / a.K, k = e - d * a.K;
+        const float wsel = __shfl(wk, k, kWave);
+        const bool local = kWave * q + lane < nent && rr[q] >= 0 && (int64_t)rr[q] < a.idx_limit;
+        const uint64_t m = __ballot(local);
+        if (local) {
+          const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
+          const long long row = a.dense ? (long long)t * a.K + k : (long long)d * a.R + rr[q];
+          pairs[pos] = Pair{row, wsel, d};
+        }
+        base += __popcll(m);
+      }
+    }
+    if (lane == 0) pair_count = base;
   }
   __syncthreads();
+  const int np = __builtin_amdgcn_readfirstlane(pair_count);
 
-  const float inv_width = (float)(1.0 / (double)P);
-  float my_inv = 0.0f;
-  if (lane < a.K) {
-    float total = 0.0f;
-    for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
-    my_inv = inv_rms(total, inv_width, a.eps);
-  }
-
-  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  float g[8];
+  unpack8(gq, g);
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    if (k < a.K) {
-      const int r = readlane_i(my_row, k);
-      const float inv = readlane_f(my_inv, k);
-      const float wk = readlane_f(my_w, k);
-      if (r >= 0 && (int64_t)r < a.num_rows && has) add_products<WBN>(xr[k], g, inv, wk, acc);
+  for (int c = 0; c < 8; ++c) g[c] = g[c] + a.gain_center;
+  const float inv_width = (float)(1.0 / (double)P);
+
+  float acc[8], comb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = comb[e] = 0.0f;
+  int next_rank = 0;  // ranks below this one have been emitted
+  auto emit_through = [&](int end_rank) {
+    while (next_rank < end_rank) {
+      const uint4 q = pack8_pz(acc);
+      if (has && a.partials) store16(a.partials + ((int64_t)next_rank * a.b + t) * P + col, q);
+      float v[8];
+      unpack8(q, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        comb[e] = comb[e] + v[e];
+        acc[e] = 0.0f;
+      }
+      ++next_rank;
     }
+  };
+
+  for (int base = 0; base < np; base += kSlots) {
+    const int nb = min(kSlots, np - base);
+    // Lane s < kSlots holds pair base + s (one LDS read for the batch).
+    Pair mine = Pair{0, 0.0f, 0};
+    if (lane < kSlots) mine = pairs[base + min(lane, nb - 1)];
+    const int row_lo = (int)(mine.row & 0xffffffffll), row_hi = (int)(mine.row >> 32);
+    uint4 xq[kSlots];
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      const long long row =
+          (long long)(((uint64_t)(uint32_t)readlane_i(row_hi, s) << 32) | (uint32_t)readlane_i(row_lo, s));
+      xq[s] = load16(a.rows + row * P + colc);
+    }
+    // All slots reduce without branches (slots past nb repeat the last
+    // pair and are never used), so the slots' butterflies interleave.
+    float ss[kSlots];
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      ss[s] = has ? chunk_ss<WBN>(xq[s], g) : 0.0f;
+      ss[s] = wave_butterfly_sum(ss[s]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s)
+        if (s < nb) block_ss[s][wave] = ss[s];
+    }
+    __syncthreads();
+    float my_inv = 0.0f;
+    if (lane < nb) {
+      float total = 0.0f;
+      for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
+      my_inv = inv_rms(total, inv_width, a.eps);
+    }
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      if (s < nb) {
+        emit_through(readlane_i(mine.rank, s));
+        const float inv = readlane_f(my_inv, s);
+        add_products<WBN>(xq[s], g, inv, readlane_f(mine.w, s), acc);
+      }
+    }
+    __syncthreads();  // block_ss is refilled by the next batch
   }
-  if (has) store16(a.out + (int64_t)t * P + col, pack8_pz(acc));
+  emit_through(a.tp);
+  if (has && a.out) store16(a.out + (int64_t)t * P + col, pack8_pz(comb));
 }
 
 template <bool WBN, bool WBF16>
-hipError_t tp_launch(const TpArgs& a, hipStream_t s) {
+hipError_t finalize_launch(const FinArgs& a, hipStream_t s) {
   const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;
-  if (a.K <= 16)
-    hipLaunchKernelGGL((tp_finalize_kernel<WBN, WBF16, 16>), dim3(a.b), dim3(kWave * nwaves), 0, s, a);
+  if (nwaves <= 8)
+    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 16, 512>), dim3(a.b), dim3(kWave * nwaves), 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((tp_finalize_kernel<WBN, WBF16, 32>), dim3(a.b), dim3(kWave * nwaves), 0, s, a);
+    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 8, 1024>), dim3(a.b), dim3(kWave * nwaves), 0,
+                       s, a);
   return hipGetLastError();
+}
+
+hipError_t finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_t s) {
+  const int key = (wbn ? 2 : 0) | (w_bf16 ? 1 : 0);
+  switch (key) {
+    case 0: return finalize_launch<false, false>(a, s);
+    case 1: return finalize_launch<false, true>(a, s);
+    case 2: return finalize_launch<true, false>(a, s);
+    default: return finalize_launch<true, true>(a, s);
+  }
+}
+
+// --------------------------------------------------- expert-TP rank sum --
+//
+// x_r = bf16(sum over ranks, in rank order from +0, of the route's
+// K-partials), one wave per (route, 512-column block): pure streaming with
+// every rank's chunk in flight at once.  Absent routes are skipped (the
+// finalize pass never reads them).
+__global__ void __launch_bounds__(256) tp_rank_sum_kernel(const uint16_t* kpart, int64_t num_rows,
+                                                          const int32_t* idx, int routes, int P,
+                                                          int tp, uint16_t* xr) {
+  const int nbk = (P + kBlockCols - 1) / kBlockCols;
+  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (wid >= (int64_t)routes * nbk) return;
+  const int route = (int)(wid / nbk);
+  const int j = (int)(wid - (int64_t)route * nbk);
+  const int r = idx[route];
+  if (r < 0 || (int64_t)r >= num_rows) return;
+  const int col = (j * kWave + (threadIdx.x & (kWave - 1))) * kChunk;
+  if (col >= P) return;
+  const uint16_t* src = kpart + (int64_t)r * P + col;
+  const int64_t rank_stride = num_rows * (int64_t)P;
+  float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  int d = 0;
+  for (; d + 8 <= tp; d += 8) {
+    uint4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = load16(src + (d + u) * rank_stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float v[8];
+      unpack8(q[u], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+    }
+  }
+  for (; d < tp; ++d) {
+    float v[8];
+    unpack8(load16(src + d * rank_stride), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+  }
+  store16(xr + (int64_t)route * P + col, pack8(sum));
 }
 
 // ------------------------------------------------------ latent combine ---
@@ -389,44 +360,22 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
 }  // namespace
 
 hipError_t launch_ep_finalize(const EpArgs& a, hipStream_t s) {
-  const int nb = (a.P + kBlockCols - 1) / kBlockCols;
-  // Fused combine when one block can hold the token's tp partials in LDS.
-  const bool fuse = a.out != nullptr && a.tp <= 8 &&
-                    (size_t)a.tp * a.P * sizeof(uint16_t) <= 64 * 1024;
-  hipError_t e;
-  switch (nb) {
-    case 1: e = ep_dispatch_nb<1>(a, fuse, s); break;
-    case 2: e = ep_dispatch_nb<2>(a, fuse, s); break;
-    case 3: e = ep_dispatch_nb<3>(a, fuse, s); break;
-    case 4: e = ep_dispatch_nb<4>(a, fuse, s); break;
-    case 5: e = ep_dispatch_nb<5>(a, fuse, s); break;
-    case 6: e = ep_dispatch_nb<6>(a, fuse, s); break;
-    case 7: e = ep_dispatch_nb<7>(a, fuse, s); break;
-    case 8: e = ep_dispatch_nb<8>(a, fuse, s); break;
-    case 9: e = ep_dispatch_nb<9>(a, fuse, s); break;
-    case 10: e = ep_dispatch_nb<10>(a, fuse, s); break;
-    case 11: e = ep_dispatch_nb<11>(a, fuse, s); break;
-    case 12: e = ep_dispatch_nb<12>(a, fuse, s); break;
-    case 13: e = ep_dispatch_nb<13>(a, fuse, s); break;
-    case 14: e = ep_dispatch_nb<14>(a, fuse, s); break;
-    case 15: e = ep_dispatch_nb<15>(a, fuse, s); break;
-    default: e = ep_dispatch_nb<16>(a, fuse, s); break;
-  }
-  if (e != hipSuccess || fuse || a.out == nullptr) return e;
-  const int64_t chunks = (int64_t)a.b * (a.P / kChunk);
-  hipLaunchKernelGGL(rank_combine_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                     a.partials, a.tp, a.b, a.P, a.out);
-  return hipGetLastError();
+  FinArgs f{a.rows, a.R, a.idx, a.R, 0, a.w, a.gamma, a.gain_center, a.eps,
+            a.b, a.K, a.P, a.tp, a.partials, a.out};
+  return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
 }
 
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
-  const int key = (a.wbn ? 2 : 0) | (a.w_bf16 ? 1 : 0);
-  switch (key) {
-    case 0: return tp_launch<false, false>(a, s);
-    case 1: return tp_launch<false, true>(a, s);
-    case 2: return tp_launch<true, false>(a, s);
-    default: return tp_launch<true, true>(a, s);
-  }
+  const int routes = a.b * a.K;
+  const int nbk = (a.P + kBlockCols - 1) / kBlockCols;
+  const int64_t waves = (int64_t)routes * nbk;
+  hipLaunchKernelGGL(tp_rank_sum_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+                     a.kpart, a.num_rows, a.idx, routes, a.P, a.tp, a.xr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FinArgs f{a.xr, 0, a.idx, a.num_rows, 1, a.w, a.gamma, a.gain_center, a.eps,
+            a.b, a.K, a.P, 1, nullptr, a.out};
+  return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
 }
 
 hipError_t launch_latent_norm(const uint16_t* lat, int tp, int b, int L, const uint16_t* gamma,

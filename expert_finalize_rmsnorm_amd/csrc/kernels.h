@@ -6,6 +6,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moetail.h"
+
+// Most (rank, route) pairs one token can have.
+#define MOETAIL_KMAX_PAIRS (MOETAIL_MAX_TP * MOETAIL_MAX_ROUTES)
+
 namespace moetail {
 
 struct EpArgs {
@@ -34,6 +39,7 @@ struct TpArgs {
   int wbn;
   int b, K, P, tp;
   uint16_t* out;          // [b][P]
+  uint16_t* xr;           // workspace [b][K][P]: rank-summed route rows
 };
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t stream);
 
@@ -42,15 +48,26 @@ hipError_t launch_latent_norm(const uint16_t* lat, int tp, int b, int L,
                               const uint16_t* gamma, float eps, uint16_t* y,
                               hipStream_t stream);
 
-// Skinny projections on the matrix cores.
+// Skinny projections on the matrix cores.  A plan fixes the K slices (and
+// so the FP32 summation order) for one (b, rows, K); forced_splits > 0
+// overrides the slice count.
 struct ProjPlan {
-  int splits;        // K slices reduced in a fixed order (1 = no partials)
-  int k_per_split;   // multiple of the k tile
+  int splits;        // K slices, partials added in slice order
+  int k_per_split;   // multiple of the 32-wide k step
+  int pitch;         // LDS row pitch of the staged activations (elements)
+  size_t lds;        // LDS bytes per block
+  int waves;         // waves per block (8 or 16), 16 weight rows each
 };
-ProjPlan plan_upproj(int b, int N, int L);
-ProjPlan plan_gate_up(int b, int I, int H);
-ProjPlan plan_down(int b, int H, int I);
-size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out);
+// Plan knobs: 0 = the library's choice.
+struct ProjTuning {
+  int splits;         // K slices
+  int waves;          // 8 or 16
+  int target_blocks;  // least blocks in the grid
+};
+// rows: weight rows of the grid (2I for gate/up), K: reduction length.
+ProjPlan plan_projection(int b, int rows, int K, const ProjTuning& t);
+// FP32 partial bytes of a plan (always: also for a single slice).
+size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always);
 
 // out[b][N] = bf16(W[N][K] . X[b][K] + rs), -0 as +0.
 hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X,

@@ -86,9 +86,8 @@ extern "C" {
  *   partials      [tp][b][P] BF16 written (the resident rank-partial
  *                 buffer), or NULL when only `out` is wanted.
  *   out           [b][P] BF16 written, or NULL for partials only.
- *   At least one of partials / out must be given.  partials may be NULL only
- *   when one block can combine the token's tp partials itself (tp <= 8 and
- *   tp * P * 2 <= 65536 bytes); otherwise MOETAIL_EUNSUPPORTED.
+ *   At least one of partials / out must be given.  The combine happens in
+ *   the same launch, so `out` never needs `partials` to be written.
  *   eps >= 0 and finite; gain_center finite.
  *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0,
  *   b <= 65535, rows_per_rank >= 1.
@@ -111,6 +110,9 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank,
  *   permuted_idx  [b][K] int32 (the same on every rank); a value outside
  *                 [0, num_rows) marks an absent route (contributes nothing).
  *   route_w       [b][K] FP32 or BF16.   gamma [P] BF16.   out [b][P] BF16.
+ *   workspace     at least moetail_workspace_bytes(MOETAIL_OP_TP_FINALIZE,
+ *                 b, K, P, 0) bytes (the rank-summed route rows x_r,
+ *                 [b][K][P] BF16), 256-byte aligned.
  *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0.
  */
 int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,
@@ -118,6 +120,7 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,
                         int route_w_dtype, const uint16_t* gamma,
                         float gain_center, float eps, int weight_before_norm,
                         int b, int K, int P, int tp, uint16_t* out,
+                        void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
 /*
@@ -171,7 +174,8 @@ int moetail_shared_expert(const uint16_t* x, int b, int H,
 
 /*
  * Workspace bytes an operation needs (0 when none):
- *   MOETAIL_OP_FINALIZE, MOETAIL_OP_TP_FINALIZE:  0
+ *   MOETAIL_OP_FINALIZE:            0
+ *   MOETAIL_OP_TP_FINALIZE:         dim0 = K, dim1 = P
  *   MOETAIL_OP_COMBINE_NORM_UPPROJ: dim0 = L, dim1 = N, dim2 = tp
  *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
  * Returns 0 for an unknown op or out-of-range sizes.

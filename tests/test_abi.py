@@ -89,19 +89,16 @@ def test_finalize_validation():
     assert _fin(K=33) == mt.EUNSUPPORTED
     assert _fin(tp=33) == mt.EUNSUPPORTED
     assert _fin(b=70000) == mt.EUNSUPPORTED
-    # combine without partials needs the token's tp partials in one block
-    assert _fin(partials=None, tp=16) == mt.EUNSUPPORTED
-    assert _fin(partials=None, tp=8, P=8192) == mt.EUNSUPPORTED
-    assert _fin(partials=None, tp=8, P=3584, b=0) == mt.OK
+    assert _fin(partials=None, tp=32, P=8192, b=0) == mt.OK
 
 
-def _tp(**kw):
+def _tp(ws=A, wsb=1 << 30, **kw):
     a = dict(kp=A, n=64, idx=A, w=A, wdt=mt.F32, gamma=A, gc=0.0, eps=1e-6, wbn=0, b=4, K=16,
              P=7168, tp=8, out=A)
     a.update(kw)
     return mt.lib().moetail_tp_finalize(a["kp"], a["n"], a["idx"], a["w"], a["wdt"], a["gamma"],
                                         a["gc"], a["eps"], a["wbn"], a["b"], a["K"], a["P"],
-                                        a["tp"], a["out"], None)
+                                        a["tp"], a["out"], ws, wsb, None)
 
 
 def test_tp_finalize_validation():
@@ -112,6 +109,9 @@ def test_tp_finalize_validation():
     assert _tp(n=0) == mt.EINVAL
     assert _tp(P=7170) == mt.EUNSUPPORTED
     assert _tp(K=40) == mt.EUNSUPPORTED
+    assert _tp(ws=None, wsb=0) == mt.EWORKSPACE
+    assert _tp(wsb=4 * 16 * 7168 * 2 - 2) == mt.EWORKSPACE
+    assert _tp(ws=A + 128) == mt.EWORKSPACE
 
 
 def _up(ws=A, wsb=1 << 30, **kw):
@@ -162,6 +162,6 @@ def test_workspace_query(b):
     sh = mt.workspace_bytes(mt.OP_SHARED_EXPERT, b, 7168, 6144)
     assert sh >= b * 6144 * 2 and sh % 256 == 0
     assert mt.workspace_bytes(mt.OP_FINALIZE, b, 3584) == 0
-    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 7168) == 0
+    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168) == b * 16 * 7168 * 2
     assert mt.workspace_bytes(99, b, 1, 1, 1) == 0
     assert mt.workspace_bytes(mt.OP_SHARED_EXPERT, 0, 7168, 6144) == 0

@@ -190,9 +190,11 @@ def test_ep_repeatable_and_graph_replay():
 # ------------------------------------------------------------- expert TP --
 
 def run_tp(inp, wbn, wkey="w32"):
-    out = empty_bf16(inp["b"], inp["P"])
+    b, K, P = inp["b"], inp["idx"].shape[1], inp["P"]
+    out = empty_bf16(b, P)
+    ws = mt.new_workspace(mt.OP_TP_FINALIZE, b, K, P)
     mt.moetail_tp_finalize(dev(inp["kpart"]), dev(inp["idx"]), dev(inp[wkey]), dev(inp["gamma"]),
-                           inp["gain_center"], inp["eps"], wbn, out)
+                           inp["gain_center"], inp["eps"], wbn, out, workspace=ws)
     return host(out)
 
 
@@ -390,3 +392,73 @@ def test_projections_graph_replay():
         torch.cuda.synchronize()
         assert np.array_equal(host(rs), eager[0]) and np.array_equal(host(out), eager[1])
     del rs_in
+
+
+def test_tail_chain_fused_combine_equals_partials_path():
+    """The rank combine done inside the finalize launch (its out row fed to
+    the up projection as a single partial) gives the same bits as writing
+    the tp partials and combining them in moetail_combine_norm_upproj."""
+    ep = workloads.ep_finalize(6)
+    up = workloads.upproj(6, b=64)
+    rows, idx, w, gamma = dev(ep["rows"]), dev(ep["idx"]), dev(ep["w32"]), dev(ep["gamma"])
+    partials, comb = empty_bf16(8, 64, 3584), empty_bf16(1, 64, 3584)
+    mt.moetail_finalize(rows, idx, w, gamma, 1.0, 1e-6, True, partials=partials)
+    mt.moetail_finalize(rows, idx, w, gamma, 1.0, 1e-6, True, out=comb[0])
+    outs = []
+    for lat, tp in ((partials, 8), (comb, 1)):
+        out, normed = empty_bf16(64, 7168), empty_bf16(64, 3584)
+        mt.moetail_combine_norm_upproj(lat, dev(up["gamma"]), 1e-6, dev(up["w_up"]), out,
+                                       normed=normed,
+                                       workspace=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, 64,
+                                                                  3584, 7168, tp))
+        outs.append((host(normed), host(out)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    want_n, _ = oracle.combine_norm_upproj(oracle.finalize(ep["rows"], ep["idx"], ep["w32"],
+                                                           ep["gamma"], 1.0, 1e-6, True,
+                                                           nthreads=NT)[0],
+                                           up["gamma"], 1e-6, up["w_up"][:64], nthreads=NT)
+    assert np.array_equal(outs[0][0], want_n)
+
+
+def test_tail_step_two_stream_graph_matches_eager():
+    """The benchmark's step: finalize on a side stream beside the shared
+    expert, joined before the up projection, captured once and replayed."""
+    ep, up, sh = workloads.ep_finalize(8), workloads.upproj(8, b=64), workloads.shared(8, b=64)
+    rows, idx, w, gamma = dev(ep["rows"]), dev(ep["idx"]), dev(ep["w32"]), dev(ep["gamma"])
+    x, wg, wu, wd = dev(sh["x"]), dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"])
+    lg, wup = dev(up["gamma"]), dev(up["w_up"])
+    lat, rs, out = empty_bf16(1, 64, 3584), empty_bf16(64, 7168), empty_bf16(64, 7168)
+    ws_sh = mt.new_workspace(mt.OP_SHARED_EXPERT, 64, 7168, 6144)
+    ws_up = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, 64, 3584, 7168, 1)
+    side = torch.cuda.Stream()
+
+    def step():
+        main = torch.cuda.current_stream()
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(fork)
+            mt.moetail_finalize(rows, idx, w, gamma, 1.0, 1e-6, True, out=lat[0])
+            join.record(side)
+        mt.moetail_shared_expert(x, wg, wu, wd, rs, workspace=ws_sh)
+        main.wait_event(join)
+        mt.moetail_combine_norm_upproj(lat, lg, 1e-6, wup, out, rs=rs, workspace=ws_up)
+
+    step()
+    eager = (host(lat), host(rs), host(out))
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    for _ in range(3):
+        for t in (lat, rs, out):
+            t.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(np.array_equal(a, b) for a, b in zip((host(lat), host(rs), host(out)), eager))
+    # and the step's latent row is the oracle's finalize + combine
+    _, want = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
+                              nthreads=NT)
+    assert np.array_equal(eager[0][0], want)

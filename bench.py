@@ -13,9 +13,10 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
   3. RMSNorm of l and the 3584 -> 7168 up projection plus rs -> out [64, 7168]
      (moetail_combine_norm_upproj with the combined row as its one partial).
 
-Each step replays a HIP graph of the three calls (the finalize on a side
-stream, concurrent with the shared expert); two input sets (weights
-and rows) alternate so that the 315 MB of weights per step stream from HBM,
+Each step replays a HIP graph of the three calls in order on one stream
+(--streams 2 puts the finalize on a side stream beside the shared expert:
+measured slower, the cross-stream fork and join inside the graph cost more
+than the overlap gains); two input sets (weights and rows) alternate so that the 315 MB of weights per step stream from HBM,
 not from the 256 MB Infinity Cache.  Inputs are resident in HBM before the
 timed region starts.  Rank 0 prints one JSON line (progress goes to stderr).
 """
@@ -56,6 +57,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-config kernel table")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
+                    help="2: the finalize on a side stream beside the shared expert; "
+                         "1: the three calls in order on one stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -105,6 +109,11 @@ def main():
     def step(d):
         """finalize runs on a side stream beside the shared expert; the up
         projection waits for both (a fork/join inside the captured graph)."""
+        if args.streams == 1:
+            finalize(d)
+            shared(d)
+            upproj(d)
+            return
         main = torch.cuda.current_stream()
         fork, join = torch.cuda.Event(), torch.cuda.Event()
         fork.record(main)
@@ -193,7 +202,8 @@ def main():
                                "expert 7168x6144 SiLU -> latent combine + RMSNorm + up "
                                "projection 3584->7168 (+rs)",
                    "b": B, "P": P, "tp": TP, "K": K, "H": H, "I": I,
-                   "global_batch": B, "parallelism": "one GPU, tp rank partials resident"},
+                   "global_batch": B, "streams": args.streams,
+                   "parallelism": "one GPU, tp rank partials resident"},
         "gpu_ms_per_step_events": round(gpu_ms, 5),
         "step_algorithmic_bytes": step_bytes,
         "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

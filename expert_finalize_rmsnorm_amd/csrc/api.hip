@@ -36,19 +36,19 @@ int check_norm_args(const void* w, int w_dtype, const uint16_t* gamma, float eps
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOETAIL_OK : MOETAIL_EHIP; }
 
-// The library's projection plans, with optional overrides read once from
-// the environment (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES and _BLOCKS
-// for KIND in UPPROJ, GATEUP, DOWN.
-int env_int(const char* name) {
+// The library's projection plans, with optional overrides read from the
+// environment at every call (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES,
+// _BLOCKS, _MR and _PF for KIND in UPPROJ, GATEUP, DOWN.  An override that
+// names no built kernel shape, or a slice that does not fit, is ignored.
+int env_int(const char* kind, const char* knob) {
+  char name[64];
+  snprintf(name, sizeof name, "MOETAIL_%s_%s", kind, knob);
   const char* v = getenv(name);
   return v ? atoi(v) : 0;
 }
 ProjTuning tuning(const char* kind) {
-  char n1[64], n2[64], n3[64];
-  snprintf(n1, sizeof n1, "MOETAIL_%s_SPLITS", kind);
-  snprintf(n2, sizeof n2, "MOETAIL_%s_WAVES", kind);
-  snprintf(n3, sizeof n3, "MOETAIL_%s_BLOCKS", kind);
-  return ProjTuning{env_int(n1), env_int(n2), env_int(n3)};
+  return ProjTuning{env_int(kind, "SPLITS"), env_int(kind, "WAVES"), env_int(kind, "BLOCKS"),
+                    env_int(kind, "MR"), env_int(kind, "PF")};
 }
 
 // The expert-TP path keeps its rank-summed route rows [b][K][P] BF16.
@@ -62,7 +62,7 @@ struct UpprojLayout {
 };
 UpprojLayout upproj_layout(int b, int L, int N) {
   UpprojLayout l;
-  l.plan = plan_projection(b, N, L, tuning("UPPROJ"));
+  l.plan = plan_projection(b, N, L, false, tuning("UPPROJ"));
   l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
   l.part_bytes = round_up(proj_partial_bytes(l.plan, b, N, false), 256);
   return l;
@@ -74,8 +74,8 @@ struct SharedLayout {
 };
 SharedLayout shared_layout(int b, int H, int I) {
   SharedLayout l;
-  l.gate_up = plan_projection(b, 2 * I, H, tuning("GATEUP"));
-  l.down = plan_projection(b, H, I, tuning("DOWN"));
+  l.gate_up = plan_projection(b, 2 * I, H, true, tuning("GATEUP"));
+  l.down = plan_projection(b, H, I, false, tuning("DOWN"));
   l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
   const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I, true);
   const size_t d = proj_partial_bytes(l.down, b, H, false);
@@ -137,6 +137,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const u
       b > MOETAIL_MAX_GEMM_TOKENS)
     return MOETAIL_EUNSUPPORTED;
   const UpprojLayout lay = upproj_layout(b, L, N);
+  if (lay.plan.splits == 0) return MOETAIL_EUNSUPPORTED;
   const size_t need = (normed ? 0 : lay.y_bytes) + lay.part_bytes;
   if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
     return MOETAIL_EWORKSPACE;
@@ -156,8 +157,11 @@ int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gat
   if (b < 0 || H <= 0 || I <= 0) return MOETAIL_EINVAL;
   if (!a16(x) || !a16(w_gate) || !a16(w_upw) || !a16(w_down) || !a16(rs)) return MOETAIL_EINVAL;
   if (h && !a16(h)) return MOETAIL_EINVAL;
-  if (H % 64 || I % 64 || b > MOETAIL_MAX_GEMM_TOKENS) return MOETAIL_EUNSUPPORTED;
+  if (H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
+      b > MOETAIL_MAX_GEMM_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
   const SharedLayout lay = shared_layout(b, H, I);
+  if (lay.gate_up.splits == 0 || lay.down.splits == 0) return MOETAIL_EUNSUPPORTED;
   const size_t need = (h ? 0 : lay.h_bytes) + lay.part_bytes;
   if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
     return MOETAIL_EWORKSPACE;
@@ -182,12 +186,14 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
       if (dim0 <= 0 || dim1 <= 0 || dim0 % 32 || dim1 % 64 || dim0 > MOETAIL_MAX_WIDTH) return 0;
       (void)dim2;
       const UpprojLayout l = upproj_layout(b, dim0, dim1);
-      return l.y_bytes + l.part_bytes;
+      return l.plan.splits ? l.y_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_SHARED_EXPERT: {
-      if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64) return 0;
+      if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64 || dim0 > MOETAIL_MAX_GEMM_K ||
+          dim1 > MOETAIL_MAX_GEMM_K)
+        return 0;
       const SharedLayout l = shared_layout(b, dim0, dim1);
-      return l.h_bytes + l.part_bytes;
+      return l.gate_up.splits && l.down.splits ? l.h_bytes + l.part_bytes : 0;
     }
     default:
       return 0;

@@ -56,16 +56,22 @@ struct ProjPlan {
   int k_per_split;   // multiple of the 32-wide k step
   int pitch;         // LDS row pitch of the staged activations (elements)
   size_t lds;        // LDS bytes per block
-  int waves;         // waves per block (8 or 16), 16 weight rows each
+  int waves;         // waves per block
+  int mr;            // 16-row tiles per wave unit (1 or 2)
+  int pf;            // k steps in flight per wave (4 or 8)
+  int blocks_per_slice;
 };
 // Plan knobs: 0 = the library's choice.
 struct ProjTuning {
-  int splits;         // K slices
-  int waves;          // 8 or 16
-  int target_blocks;  // least blocks in the grid
+  int splits;         // K slices (a power of two)
+  int waves;          // waves per block
+  int target_blocks;  // blocks in the grid (default: one per CU)
+  int mr;             // tiles per wave unit
+  int pf;             // prefetch depth
 };
-// rows: weight rows of the grid (2I for gate/up), K: reduction length.
-ProjPlan plan_projection(int b, int rows, int K, const ProjTuning& t);
+// rows: weight rows of the grid (2I for gate/up), K: reduction length;
+// always_partials: the epilogue needs the reduction kernel even unsplit.
+ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const ProjTuning& t);
 // FP32 partial bytes of a plan (always: also for a single slice).
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always);
 

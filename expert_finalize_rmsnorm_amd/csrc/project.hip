@@ -34,7 +34,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKStep = 32;              // k per MFMA
 constexpr int kLdsBytes = 160 * 1024;   // gfx950 LDS available to one block
-constexpr int kPF = 8;                  // k steps in flight per wave
 
 enum { kLinear = 0, kGateUp = 1 };
 
@@ -45,6 +44,7 @@ struct FxArgs {
   const uint16_t* X;   // [b][K]
   int b;
   int k_per_split;
+  int blocks_per_slice;
   int pitch;           // LDS row pitch of the staged activations (elements)
   float* partials;     // [splits][b][N], or null for the direct epilogue
   const uint16_t* rs;  // direct epilogue only: [b][N] or null
@@ -69,34 +69,60 @@ __device__ __forceinline__ uint2 pack4_pz(float a, float b, float c, float d) {
   return make_uint2(pack2_rn_pz(a, b), pack2_rn_pz(c, d));
 }
 
-// kWaves waves per block, 16 weight rows each.
-template <int NT, int kWaves>
-__global__ void __launch_bounds__(kWave * kWaves) fx_kernel(FxArgs a) {
+// One block per CU, kWaves waves per block.  Block g works on K slice
+// s = g / blocks_per_slice; its waves take units u, u + stride, ... of the
+// slice (u = wave index within the slice, stride = waves per slice), a unit
+// being MR consecutive 16-row tiles that share every activation fragment
+// read from LDS.  The slice's activations are staged in LDS once per block
+// and reused for every unit the block streams.  Each wave's (unit, k step)
+// sequence is one flat stream: the kPF-deep prefetch ring runs across unit
+// boundaries, and a unit's FP32 result leaves as soon as its last step is in.
+template <int NT, int MR, int kPF, int kWaves>
+__global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
   extern __shared__ uint16_t xs[];  // [16 * NT][pitch]
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15;
   const int kq = lane >> 4;
   const int K = a.K;
-  const int kb = blockIdx.y * a.k_per_split;
+  const int slice = blockIdx.x / a.blocks_per_slice;
+  const int kb = slice * a.k_per_split;
   const int ke = min(K, kb + a.k_per_split);
   const int nsteps = (ke - kb) / kKStep;
-  const int row0 = (blockIdx.x * kWaves + wave) * 16;
-  const bool active = row0 < a.N;  // wave-uniform
+  const int stride = a.blocks_per_slice * kWaves;
+  const int u = (blockIdx.x - slice * a.blocks_per_slice) * kWaves + wave;
+  const int nunits = a.N / (16 * MR);
+  const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // wave-uniform
+  const int total = my_units * nsteps;
 
-  // The wave's 16 weight rows lie in one matrix (n0 % 16 == 0).
-  const uint16_t* pa = nullptr;
-  if (active) {
+  // The MR tiles of a unit lie in one matrix (n0 % (16 * MR) == 0).
+  auto unit_ptr = [&](int unit) {
+    const int row0 = unit * 16 * MR;
     const uint16_t* base = row0 < a.n0 ? a.A0 + (int64_t)row0 * K
                                        : a.A1 + (int64_t)(row0 - a.n0) * K;
-    pa = base + (int64_t)lrow * K + kb + 8 * kq;
-  }
-  uint4 ra[kPF];
-  const int last = nsteps - 1;
-  auto load_a = [&](int j) { return load16(pa + min(j, last) * kKStep); };
-  if (active) {
+    return base + (int64_t)lrow * K + kb + 8 * kq;
+  };
+
+  // Load cursor: (unit, step); past the wave's last step it stays on it
+  // (cache hits), so every ring slot is refilled unconditionally.
+  int l_step = 0, l_left = total, l_unit = u;
+  const uint16_t* l_ptr = total > 0 ? unit_ptr(u) : a.A0;
+  auto next_load = [&](uint4 (&q)[MR]) {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) ra[i] = load_a(i);
+    for (int m = 0; m < MR; ++m) q[m] = load16(l_ptr + (int64_t)m * 16 * K + l_step * kKStep);
+    if (l_left > 1) {
+      --l_left;
+      if (++l_step == nsteps) {
+        l_step = 0;
+        l_unit += stride;
+        l_ptr = unit_ptr(l_unit);
+      }
+    }
+  };
+  uint4 ra[kPF][MR];
+  if (total > 0) {
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) next_load(ra[i]);
   }
 
   // Stage X[16*NT][kb, ke) in LDS; padded tokens repeat the last real one.
@@ -110,48 +136,66 @@ __global__ void __launch_bounds__(kWave * kWaves) fx_kernel(FxArgs a) {
         load16(a.X + (int64_t)src * K + kb + pc * 8);
   }
   __syncthreads();
-  if (!active) return;
+  if (total == 0) return;
 
-  f32x4_t acc[NT];
+  f32x4_t acc[MR][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[m][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const uint16_t* xl = xs + lrow * a.pitch + 8 * kq;
-  for (int j0 = 0; j0 < nsteps; j0 += kPF) {
+  int c_unit = u, c_step = 0;
+
+  // Accumulator lane layout: rows 16 * tile + 4 * (lane / 16) + v, token lane % 16.
+  auto emit = [&]() {
 #pragma unroll
-    for (int i = 0; i < kPF; ++i) {
-      const int j = j0 + i;
-      if (j < nsteps) {
+    for (int m = 0; m < MR; ++m) {
+      const int r = (c_unit * MR + m) * 16 + 4 * kq;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const uint4 bq = *reinterpret_cast<const uint4*>(xl + 16 * nt * a.pitch + j * kKStep);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ra[i]),
-                                                            __builtin_bit_cast(bf16x8_t, bq),
-                                                            acc[nt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tok = 16 * nt + lrow;
+        const f32x4_t s = acc[m][nt];
+        acc[m][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (tok >= a.b) continue;
+        if (a.partials) {
+          *reinterpret_cast<f32x4_t*>(a.partials + ((int64_t)slice * a.b + tok) * a.N + r) = s;
+        } else {
+          float o[4] = {s[0], s[1], s[2], s[3]};
+          if (a.rs) {
+            const uint2 q2 = *reinterpret_cast<const uint2*>(a.rs + (int64_t)tok * a.N + r);
+            o[0] = o[0] + bf16_lo(q2.x);
+            o[1] = o[1] + bf16_hi(q2.x);
+            o[2] = o[2] + bf16_lo(q2.y);
+            o[3] = o[3] + bf16_hi(q2.y);
+          }
+          *reinterpret_cast<uint2*>(a.out + (int64_t)tok * a.N + r) =
+              pack4_pz(o[0], o[1], o[2], o[3]);
         }
       }
-      ra[i] = load_a(j + kPF);
     }
-  }
+  };
 
-  // Accumulator lane layout: rows row0 + 4 * (lane / 16) + v, token lane % 16.
-  const int r = row0 + 4 * kq;
+  for (int q0 = 0; q0 < total; q0 += kPF) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int tok = 16 * nt + lrow;
-    if (tok >= a.b) continue;
-    const f32x4_t s = acc[nt];
-    if (a.partials) {
-      *reinterpret_cast<f32x4_t*>(a.partials + ((int64_t)blockIdx.y * a.b + tok) * a.N + r) = s;
-    } else {
-      float o[4] = {s[0], s[1], s[2], s[3]};
-      if (a.rs) {
-        const uint2 q2 = *reinterpret_cast<const uint2*>(a.rs + (int64_t)tok * a.N + r);
-        o[0] = o[0] + bf16_lo(q2.x);
-        o[1] = o[1] + bf16_hi(q2.x);
-        o[2] = o[2] + bf16_lo(q2.y);
-        o[3] = o[3] + bf16_hi(q2.y);
+    for (int i = 0; i < kPF; ++i) {
+      if (q0 + i < total) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint4 bq =
+              *reinterpret_cast<const uint4*>(xl + 16 * nt * a.pitch + c_step * kKStep);
+#pragma unroll
+          for (int m = 0; m < MR; ++m)
+            acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ra[i][m]), __builtin_bit_cast(bf16x8_t, bq),
+                acc[m][nt], 0, 0, 0);
+        }
+        if (++c_step == nsteps) {
+          emit();
+          c_step = 0;
+          c_unit += stride;
+        }
       }
-      *reinterpret_cast<uint2*>(a.out + (int64_t)tok * a.N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
+      next_load(ra[i]);
     }
   }
 }
@@ -200,85 +244,128 @@ int token_blocks(int b) {
 
 int round_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
-// Slices of K: each slice's staged activations fit the LDS (row pitch
-// rounded to 128 + 8 elements keeps the LDS reads conflict-free); at least
-// `target` blocks when target > 0; forced_splits > 0 asks for that many
-// slices (raised to what the LDS needs, capped at 4 k steps per slice).
-ProjPlan make_plan(int b, int rows, int K, int waves, int target, int forced_splits) {
-  const int tok = 16 * token_blocks(b);
-  const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
-  const int row_blocks = (rows + 16 * waves - 1) / (16 * waves);
-  const int lds_min = (K + kmax - 1) / kmax;
-  int splits = lds_min;
-  const int par = target > 0 ? (target + row_blocks - 1) / row_blocks : 1;
-  if (par > splits) splits = par;
-  if (forced_splits > splits) splits = forced_splits;
-  const int max_splits = K / (kKStep * 4);  // at least 4 k steps per slice
-  if (splits > max_splits) splits = max_splits > 0 ? max_splits : 1;
-  int kps = round_up_i((K + splits - 1) / splits, kKStep);
-  while (round_up_i(kps, 128) > kmax && kps > kKStep) kps -= kKStep;  // stay inside LDS
-  splits = (K + kps - 1) / kps;
-  ProjPlan p;
-  p.splits = splits;
-  p.k_per_split = kps;
-  p.pitch = round_up_i(kps, 128) + 8;
-  p.lds = (size_t)tok * p.pitch * sizeof(uint16_t);
-  p.waves = waves;
-  return p;
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
 }
 
-template <int NT, int W>
-hipError_t fx_launch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+// The plan: `blocks` blocks (one per CU) split over `splits` K slices; each
+// slice's activations must fit the LDS (row pitch rounded to 128 + 8
+// elements keeps the LDS reads conflict-free).  Without overrides the slice
+// count and waves per block are chosen to minimize the modelled bytes: the
+// weight stream including idle waves of an uneven tile split and a per-tile
+// overhead, the staged activations (once per block), and the FP32 partials
+// (written and re-read) with the reduction launch.
+// The kernel shapes built: (tiles per unit, prefetch depth, waves per block).
+struct Shape {
+  int mr, pf, waves;
+};
+constexpr Shape kShapes[] = {{1, 8, 7},  {1, 8, 8},  {1, 8, 14}, {1, 8, 16}, {2, 4, 4},
+                             {2, 4, 7},  {2, 4, 8},  {2, 8, 4},  {2, 8, 7},  {2, 8, 8}};
+
+ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
+  const int tok = 16 * token_blocks(b);
+  const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
+  const int blocks = t.target_blocks > 0 ? t.target_blocks : cu_count();
+  double best = 1e300;
+  ProjPlan p{};
+  for (int splits = 1; splits <= 64; splits *= 2) {
+    if (t.splits > 0 && splits != t.splits) continue;
+    int kps = round_up_i((K + splits - 1) / splits, kKStep);
+    if (round_up_i(kps, 128) > kmax) continue;  // slice does not fit the LDS
+    if (kps < kKStep * 4 && splits > 1) continue;
+    const int real_splits = (K + kps - 1) / kps;
+    const int bps = (blocks + real_splits - 1) / real_splits;
+    for (const Shape& sh : kShapes) {
+      if (t.waves > 0 && sh.waves != t.waves) continue;
+      if (t.mr > 0 ? sh.mr != t.mr : sh.mr != 1) continue;
+      if (t.pf > 0 && sh.pf != t.pf) continue;
+      if (rows % (16 * sh.mr)) continue;
+      const int w = sh.waves;
+      const int units = rows / (16 * sh.mr);
+      const double per_wave = (double)((units + bps * w - 1) / (bps * w));
+      // a unit's epilogue and ring refill cost about 4 k steps
+      const double a_bytes =
+          per_wave * bps * w * 16.0 * sh.mr * (kps + 4 * kKStep) * 2.0 * real_splits;
+      const double x_bytes = (double)blocks * tok * kps * 2.0;
+      // partials written and re-read, plus the reduction launch (~4 us)
+      const double p_bytes = (real_splits > 1 || always_partials)
+                                 ? real_splits * (double)b * rows * 4.0 * 2.0 + 16.0e6 : 0.0;
+      const double cost = a_bytes + x_bytes + p_bytes;
+      if (cost < best * 0.999) {
+        best = cost;
+        p.splits = real_splits;
+        p.k_per_split = kps;
+        p.pitch = round_up_i(kps, 128) + 8;
+        p.lds = (size_t)tok * p.pitch * sizeof(uint16_t);
+        p.waves = w;
+        p.mr = sh.mr;
+        p.pf = sh.pf;
+        p.blocks_per_slice = bps;
+      }
+    }
+  }
+  if (best == 1e300 && (t.splits > 0 || t.waves > 0 || t.mr > 0 || t.pf > 0)) {
+    // an override that cannot fit: the best plan without it
+    const ProjTuning free_t{0, 0, t.target_blocks, 0, 0};
+    return make_plan(b, rows, K, always_partials, free_t);
+  }
+  return p;  // splits == 0: no slice of K fits the LDS
+}
+
+template <int NT, int MR, int PF, int W>
+hipError_t px_launch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   static bool attr_set = false;  // idempotent: every call sets the same maximum
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fx_kernel<NT, W>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_kernel<NT, MR, PF, W>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int row_blocks = (a.N + 16 * W - 1) / (16 * W);
-  hipLaunchKernelGGL((fx_kernel<NT, W>), dim3(row_blocks, p.splits), dim3(kWave * W), p.lds, s, a);
+  hipLaunchKernelGGL((px_kernel<NT, MR, PF, W>), dim3(p.splits * p.blocks_per_slice),
+                     dim3(kWave * W), p.lds, s, a);
   return hipGetLastError();
 }
 
-template <int W>
-hipError_t fx_dispatch_w(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+template <int MR, int PF, int W>
+hipError_t px_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   switch (token_blocks(a.b)) {
-    case 1: return fx_launch<1, W>(a, p, s);
-    case 2: return fx_launch<2, W>(a, p, s);
-    case 4: return fx_launch<4, W>(a, p, s);
-    default: return fx_launch<8, W>(a, p, s);
+    case 1: return px_launch<1, MR, PF, W>(a, p, s);
+    case 2: return px_launch<2, MR, PF, W>(a, p, s);
+    case 4: return px_launch<4, MR, PF, W>(a, p, s);
+    default: return px_launch<8, MR, PF, W>(a, p, s);
   }
 }
 
 hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
-  return p.waves == 16 ? fx_dispatch_w<16>(a, p, s) : fx_dispatch_w<8>(a, p, s);
+  const int key = p.mr * 1000 + p.pf * 100 + p.waves;
+  switch (key) {
+    case 1807: return px_dispatch_nt<1, 8, 7>(a, p, s);
+    case 1808: return px_dispatch_nt<1, 8, 8>(a, p, s);
+    case 1814: return px_dispatch_nt<1, 8, 14>(a, p, s);
+    case 1816: return px_dispatch_nt<1, 8, 16>(a, p, s);
+    case 2404: return px_dispatch_nt<2, 4, 4>(a, p, s);
+    case 2407: return px_dispatch_nt<2, 4, 7>(a, p, s);
+    case 2408: return px_dispatch_nt<2, 4, 8>(a, p, s);
+    case 2804: return px_dispatch_nt<2, 8, 4>(a, p, s);
+    case 2807: return px_dispatch_nt<2, 8, 7>(a, p, s);
+    case 2808: return px_dispatch_nt<2, 8, 8>(a, p, s);
+    default: return hipErrorInvalidValue;  // not a shape of kShapes
+  }
 }
 
 }  // namespace
 
-// Default knobs, from a sweep on MI355X of slices {2,3,4,6,8,12} x waves
-// {8,16} at b in {16,32,64,128} for the three projections of the tail
-// (gate/up 12288x7168, down 7168x6144, up 7168x3584): four K slices win
-// almost everywhere (eight for the long reductions at b = 64), and 16 waves
-// per block for the long reductions (gate/up always, down above b = 32)
-// and for every projection above b = 64.
-ProjTuning default_tuning(int b, int rows, int K) {
-  const bool wide = K >= 6144;
-  ProjTuning t{4, 8, 0};
-  if (wide && (rows >= 12288 || b > 32)) t.waves = 16;
-  if (b > 64) t.waves = 16;
-  if (wide && b > 32 && b <= 64) t.splits = 8;
-  if (b > 64 && !wide) t.splits = 3;
-  return t;
-}
-
-ProjPlan plan_projection(int b, int rows, int K, const ProjTuning& t) {
-  const ProjTuning d = default_tuning(b, rows, K);
-  const int splits = t.splits > 0 ? t.splits : d.splits;
-  const int waves = (t.waves > 0 ? t.waves : d.waves) == 16 ? 16 : 8;
-  const int target = t.target_blocks > 0 ? t.target_blocks : 0;
-  return make_plan(b, rows, K, waves, target, splits);
+ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
+  return make_plan(b, rows, K, always_partials, t);
 }
 
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
@@ -289,8 +376,8 @@ hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X, int
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
   const bool split = plan.splits > 1;
-  FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.pitch, split ? partials : nullptr,
-           rs, out};
+  FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
+           split ? partials : nullptr, rs, out};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess || !split) return e;
   const int64_t threads = (int64_t)b * (N / 4);
@@ -303,7 +390,8 @@ hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int I, int H, 
                           int b, uint16_t* h, const ProjPlan& plan, float* partials,
                           hipStream_t s) {
   // Gate rows [0, I) and up rows [I, 2I) in one grid; SiLU in the reduction.
-  FxArgs a{Wg, Wu, I, 2 * I, H, X, b, plan.k_per_split, plan.pitch, partials, nullptr, nullptr};
+  FxArgs a{Wg, Wu, I, 2 * I, H, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
+           partials, nullptr, nullptr};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess) return e;
   const int64_t threads = (int64_t)b * (I / 4);

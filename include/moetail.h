@@ -64,6 +64,7 @@ extern "C" {
 #define MOETAIL_MAX_ROUTES 32   /* K */
 #define MOETAIL_MAX_TOKENS 65535
 #define MOETAIL_MAX_GEMM_TOKENS 128 /* b of the two projections */
+#define MOETAIL_MAX_GEMM_K 32768    /* H and I of the shared expert */
 
 /*
  * EP finalize ([tail] module docstring, "With expert parallelism ..."):
@@ -164,7 +165,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp,
  *   rs      [b][H] BF16 written (the input of moetail_combine_norm_upproj).
  *   workspace at least moetail_workspace_bytes(MOETAIL_OP_SHARED_EXPERT,
  *           b, H, I, 0) bytes, 256-byte aligned.
- *   Limits: b <= 128, H % 64 == 0, I % 64 == 0, H, I >= 64.
+ *   Limits: b <= 128, H % 64 == 0, I % 64 == 0, 64 <= H, I <= MOETAIL_MAX_GEMM_K.
  */
 int moetail_shared_expert(const uint16_t* x, int b, int H,
                           const uint16_t* w_gate, const uint16_t* w_upw, int I,

@@ -333,7 +333,8 @@ def test_shared_scale(b):
     assert np.array_equal(got_rs2, got_rs)
 
 
-@pytest.mark.parametrize("b,H,I", [(5, 512, 256), (33, 256, 128), (1, 64, 64), (128, 128, 192)])
+@pytest.mark.parametrize("b,H,I", [(5, 512, 256), (33, 256, 128), (1, 64, 64), (128, 128, 192),
+                                   (128, 32768, 64), (3, 64, 32768)])
 def test_shared_small_full(b, H, I):
     inp = workloads.shared(b + H, b=b, H=H, I=I)
     want_h, want_rs = oracle.shared_expert(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"],
@@ -362,6 +363,37 @@ def test_shared_unit_rows():
     assert np.array_equal(got_rs, got_h[:, sel])  # one exact product per output
     zh, zrs = run_shared(dict(inp, x=np.zeros_like(x)))
     assert not zh.any() and not zrs.any()
+
+
+PLAN_OVERRIDES = [dict(WAVES=w, SPLITS=s) for w in (7, 8, 14, 16) for s in (2, 8)] + [
+    dict(MR=2, PF=f, WAVES=w, SPLITS=s) for f in (4, 8) for w in (4, 7, 8) for s in (2, 8)] + [
+    dict(WAVES=8, SPLITS=2, BLOCKS=100), dict(WAVES=14, SPLITS=8, BLOCKS=37),
+    dict(MR=2, PF=4, WAVES=7, SPLITS=8, BLOCKS=37), dict(SPLITS=1)]
+
+
+@pytest.mark.parametrize("b", [1, 40, 128])
+def test_projection_plan_overrides(b, monkeypatch):
+    """Every kernel shape the plan can pick (waves per block, slice count,
+    uneven blocks per slice) against the oracle, through the tuning
+    overrides; a slice count that does not fit falls back to the default."""
+    up = workloads.upproj(70 + b, b=b, tp=2, L=3584, N=512, with_rs=True)
+    sh = workloads.shared(80 + b, b=b, H=1024, I=1024)
+    want_up = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"], up["rs"],
+                                         nthreads=NT)[1]
+    want_h, want_rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                           nthreads=NT)
+    for ov in PLAN_OVERRIDES:
+        for kind in ("UPPROJ", "GATEUP", "DOWN"):
+            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF"):
+                if key in ov:
+                    monkeypatch.setenv(f"MOETAIL_{kind}_{key}", str(ov[key]))
+                else:
+                    monkeypatch.delenv(f"MOETAIL_{kind}_{key}", raising=False)
+        _, got_up = run_upproj(up, rs=up["rs"])
+        gemm_bar(got_up, want_up, f"upproj b={b} {ov}")
+        got_h, got_rs = run_shared(sh)
+        gemm_bar(got_h, want_h, f"h b={b} {ov}")
+        gemm_bar(got_rs, want_rs, f"rs b={b} {ov}")
 
 
 def test_projections_graph_replay():

@@ -6,12 +6,11 @@
 A step is one pass of the whole tail at b=64 tokens, P=3584:
 
   1. EP finalize of tp=8 simulated ranks' GEMM2 rows (top-16 routes, 2 local
-     per rank): each rank's BF16 partial, combined in rank order in the same
-     launch into the latent row l [64, 3584] (the partials stay on chip);
+     per rank) into each rank's BF16 latent partial [8, 64, 3584];
   2. the shared expert 7168 -> 6144 (gate/up, SiLU) -> 7168 into the
      reduce-scatter partial rs [64, 7168];
-  3. RMSNorm of l and the 3584 -> 7168 up projection plus rs -> out [64, 7168]
-     (moetail_combine_norm_upproj with the combined row as its one partial).
+  3. the rank-order combine of the 8 partials, RMSNorm, and the 3584 -> 7168
+     up projection plus rs -> out [64, 7168] (moetail_combine_norm_upproj).
 
 Each step replays a HIP graph of the three calls in order on one stream
 (--streams 2 puts the finalize on a side stream beside the shared expert:
@@ -44,9 +43,9 @@ def log(msg):
 def algorithmic_bytes():
     """Bytes each call must move at least (inputs read once, outputs written
     once), per entry point of the step."""
-    fin = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2 + B * P * 2
+    fin = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2 + TP * B * P * 2
     shared = 3 * H * I * 2 + B * H * 2 + B * H * 2
-    upproj = B * P * 2 + P * 2 + H * P * 2 + B * H * 2 + B * H * 2
+    upproj = TP * B * P * 2 + P * 2 + H * P * 2 + B * H * 2 + B * H * 2
     return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj)
 
 
@@ -84,18 +83,18 @@ def main():
                  gamma=dev(ep["gamma"]), x=dev(sh["x"]), wg=dev(sh["w_gate"]),
                  wu=dev(sh["w_up"]), wd=dev(sh["w_down"]), lgamma=dev(up["gamma"]),
                  w_up=dev(up["w_up"]),
-                 lat=torch.empty((1, B, P), dtype=torch.int16, device="cuda"),
+                 lat=torch.empty((TP, B, P), dtype=torch.int16, device="cuda"),
                  rs=torch.empty((B, H), dtype=torch.int16, device="cuda"),
                  out=torch.empty((B, H), dtype=torch.int16, device="cuda"),
                  ws_sh=mt.new_workspace(mt.OP_SHARED_EXPERT, B, H, I),
-                 ws_up=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, B, P, H, 1),
+                 ws_up=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, B, P, H, TP),
                  host=(ep, up, sh) if s == 0 else None)
         sets.append(d)
     torch.cuda.synchronize()
 
     def finalize(d):
         mt.moetail_finalize(d["rows"], d["idx"], d["w"], d["gamma"], 1.0, 1e-6, True,
-                            out=d["lat"][0])
+                            partials=d["lat"])
 
     def shared(d):
         mt.moetail_shared_expert(d["x"], d["wg"], d["wu"], d["wd"], d["rs"], workspace=d["ws_sh"])
@@ -277,6 +276,10 @@ def config_kernels(base, log):
                                              1.0, 1e-6, True, out=out), 48)
     add("finalize+combine b=64, out only (partials not written)", us, fin_in + B * P * 2,
         tokens_per_s=round(B / (us * 1e-6), 1))
+    us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], base["gamma"],
+                                             1.0, 1e-6, True, partials=part), 48)
+    add("finalize b=64, partials only", us, fin_in + TP * B * P * 2,
+        tokens_per_s=round(B / (us * 1e-6), 1))
     del rows
 
     # expert-TP finalize: b=128, K=16, P=7168, tp=8 (235 MB of K-partials)
@@ -330,9 +333,8 @@ def cpu_baseline(host_inputs, log):
     ep, up, sh = host_inputs
     threads = max(1, min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    _, lat = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
-                             nthreads=threads)
-    lat = lat[None]
+    lat, _ = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
+                             combine=False, nthreads=threads)
     _, rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
                                  nthreads=threads)
     oracle.combine_norm_upproj(lat, up["gamma"], 1e-6, up["w_up"], rs, nthreads=threads)

@@ -29,17 +29,27 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// A -0 BF16 word (0x8000) leaves as +0.
-__device__ __forceinline__ uint32_t plus_zero16(uint32_t h) { return h == 0x8000u ? 0u : h; }
-
-// Two FP32 values -> one word of two BF16 (low column in the low half),
-// each rounded to nearest even with -0 written as +0.
-__device__ __forceinline__ uint32_t pack2_rn_pz(float lo, float hi) {
-  return plus_zero16(bf16_bits(lo)) | (plus_zero16(bf16_bits(hi)) << 16);
-}
-// Same without the -0 rule (for values that stay inside a kernel).
+// Two FP32 values -> one word of two BF16 (low column in the low half) in
+// one v_cvt_pk_bf16_f32.  The instruction rounds to nearest even, keeps
+// denormals, and returns a NaN's upper half with the quiet bit set: on every
+// one of the 2^32 inputs it gives the bits of bf16_bits above.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_rn(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// A -0 BF16 half (0x8000) leaves as +0.
+__device__ __forceinline__ uint32_t plus_zero2(uint32_t w) {
+  const uint32_t lo = (w & 0x7fffu) ? (w & 0xffffu) : 0u;
+  const uint32_t hi = (w & 0x7fff0000u) ? (w & 0xffff0000u) : 0u;
+  return lo | hi;
+}
+
+// pack2_rn with -0 written as +0 (for every BF16 word that leaves a kernel).
+__device__ __forceinline__ uint32_t pack2_rn_pz(float lo, float hi) {
+  return plus_zero2(pack2_rn(lo, hi));
 }
 
 // 16 bytes = 8 BF16 columns <-> 8 FP32.

@@ -104,6 +104,8 @@ struct FinArgs {
   int b, K, P, tp;
   uint16_t* partials;   // [tp][b][P] or null
   uint16_t* out;        // [b][P] or null
+  int wpq;              // waves per column group: block (t, q) forms the
+                        // products of waves [q * wpq, (q + 1) * wpq)
 };
 
 struct Pair {
@@ -124,6 +126,9 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
   const int nwaves = blockDim.x / kWave;
   const int t = blockIdx.x;
   const int P = a.P;
+  // Every block of token t takes the whole row's sums of squares; only the
+  // waves of its column group go on to the products.
+  const bool prod = wave / a.wpq == (int)blockIdx.y;  // wave-uniform
 
   // Wave 0 lists the local (rank, route) pairs.  Entry e = d * K + k (rank
   // major, route minor: the order of the sums); lane l holds entries l,
@@ -227,29 +232,38 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
       for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
       my_inv = inv_rms(total, inv_width, a.eps);
     }
+    if (prod) {
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      if (s < nb) {
-        emit_through(readlane_i(mine.rank, s));
-        const float inv = readlane_f(my_inv, s);
-        add_products<WBN>(xq[s], g, inv, readlane_f(mine.w, s), acc);
+      for (int s = 0; s < kSlots; ++s) {
+        if (s < nb) {
+          emit_through(readlane_i(mine.rank, s));
+          const float inv = readlane_f(my_inv, s);
+          add_products<WBN>(xq[s], g, inv, readlane_f(mine.w, s), acc);
+        }
       }
     }
     __syncthreads();  // block_ss is refilled by the next batch
   }
+  if (!prod) return;
   emit_through(a.tp);
   if (has && a.out) store16(a.out + (int64_t)t * P + col, pack8_pz(comb));
 }
 
+// Column groups per token: enough blocks for one per CU (a block holds
+// a CU: up to 16 waves of up to 209 VGPRs), at most one group per wave.
 template <bool WBN, bool WBF16>
-hipError_t finalize_launch(const FinArgs& a, hipStream_t s) {
+hipError_t finalize_launch(FinArgs a, hipStream_t s) {
   const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;
+  const int want = (device_cu_count() + a.b - 1) / a.b;
+  const int groups = want < 1 ? 1 : want > nwaves ? nwaves : want;
+  a.wpq = (nwaves + groups - 1) / groups;
+  const dim3 grid(a.b, (nwaves + a.wpq - 1) / a.wpq);
   if (nwaves <= 8)
-    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 16, 512>), dim3(a.b), dim3(kWave * nwaves), 0,
-                       s, a);
+    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 16, 512>), grid, dim3(kWave * nwaves), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 8, 1024>), dim3(a.b), dim3(kWave * nwaves), 0,
-                       s, a);
+    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 8, 1024>), grid, dim3(kWave * nwaves), 0, s,
+                       a);
   return hipGetLastError();
 }
 
@@ -260,6 +274,154 @@ hipError_t finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_
     case 1: return finalize_launch<false, true>(a, s);
     case 2: return finalize_launch<true, false>(a, s);
     default: return finalize_launch<true, true>(a, s);
+  }
+}
+
+// ------------------------------------------------ per-rank finalize -----
+//
+// The same arithmetic when only the rank partials are asked for: one block
+// per (token t, rank d), one wave per 512-column block.  Each wave lists the
+// rank's local routes itself (lane k < K reads idx[d][t][k]; one ballot;
+// the set bits in ascending order are the routes in the order of the sum),
+// so no LDS pass or barrier precedes the row loads.  A block reads only its
+// rank's rows, so a token's rows spread over tp blocks.  The partial is the
+// fused kernel's bit for bit: the same chunks, tree, inverse and route order.
+template <bool WBN, bool WBF16, int kSlots, int kMaxThreads>
+__global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
+  __shared__ float block_ss[kSlots][16];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwaves = blockDim.x / kWave;
+  const int t = blockIdx.x;
+  const int d = blockIdx.y;
+  const int P = a.P;
+  const int col = (wave * kWave + lane) * kChunk;
+  const bool has = col < P;
+  const int colc = has ? col : P - kChunk;
+  const uint4 gq = load16(a.gamma + colc);
+  int e = -1;
+  float wk = 0.0f;
+  if (lane < a.K) {
+    e = a.idx[((int64_t)d * a.b + t) * a.K + lane];
+    wk = load_weight<WBF16>(a.w, (int64_t)t * a.K + lane);
+  }
+  uint64_t mask = __ballot(lane < a.K && e >= 0 && (int64_t)e < a.idx_limit);
+  const int np = __popcll(mask);
+
+  float g[8];
+  unpack8(gq, g);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) g[c] = g[c] + a.gain_center;
+  const float inv_width = (float)(1.0 / (double)P);
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+  const uint16_t* rank_rows = a.rows + (int64_t)d * a.R * P;
+
+  for (int base = 0; base < np; base += kSlots) {
+    const int nb = min(kSlots, np - base);
+    int ks[kSlots];
+    uint4 xq[kSlots];
+    uint64_t m = mask;
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      // Slot s takes the next local route; slots past nb repeat the last.
+      ks[s] = m ? (int)__builtin_ctzll(m) : (s > 0 ? ks[s - 1] : 0);
+      if (m) m &= m - 1;
+      const int row = readlane_i(e, ks[s]);
+      xq[s] = load16(rank_rows + (int64_t)row * P + colc);
+    }
+    mask = m;
+    float ss[kSlots];
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      ss[s] = has ? chunk_ss<WBN>(xq[s], g) : 0.0f;
+      ss[s] = wave_butterfly_sum(ss[s]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s)
+        if (s < nb) block_ss[s][wave] = ss[s];
+    }
+    __syncthreads();
+    float my_inv = 0.0f;
+    if (lane < nb) {
+      float total = 0.0f;
+      for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
+      my_inv = inv_rms(total, inv_width, a.eps);
+    }
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+      if (s < nb)
+        add_products<WBN>(xq[s], g, readlane_f(my_inv, s), readlane_f(wk, ks[s]), acc);
+    }
+    __syncthreads();  // block_ss is refilled by the next batch
+  }
+  if (has) store16(a.partials + ((int64_t)d * a.b + t) * P + col, pack8_pz(acc));
+}
+
+// out[t] = bf16(sum over ranks, in rank order from +0, of partials[d][t]),
+// -0 as +0; one thread per 8 columns of a token, every rank's load in
+// flight at once.
+__global__ void __launch_bounds__(256) rank_combine_kernel(const uint16_t* partials, int tp, int b,
+                                                           int P, uint16_t* out) {
+  const int per_tok = P / kChunk;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)b * per_tok) return;
+  const int t = (int)(i / per_tok);
+  const int col = (int)(i - (int64_t)t * per_tok) * kChunk;
+  const uint16_t* src = partials + (int64_t)t * P + col;
+  const int64_t rank_stride = (int64_t)b * P;
+  float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int d0 = 0; d0 < tp; d0 += 8) {
+    uint4 q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = load16(src + min(d0 + u, tp - 1) * rank_stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (d0 + u < tp) {
+        float v[8];
+        unpack8(q[u], v);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sum[c] = sum[c] + v[c];
+      }
+    }
+  }
+  store16(out + (int64_t)t * P + col, pack8_pz(sum));
+}
+
+// Rows in flight per batch: the expected local routes of a rank (K / tp),
+// as 4, 8 or 16 slots (8 at most for rows wider than 4096 columns, whose
+// 16-wave blocks leave 128 VGPRs a lane); a rank holding more takes more
+// batches.
+template <bool WBN, bool WBF16>
+hipError_t rank_finalize_launch(const FinArgs& a, hipStream_t s) {
+  const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;
+  const int expect = (a.K + a.tp - 1) / a.tp;
+  const dim3 grid(a.b, a.tp), block(kWave * nwaves);
+  if (nwaves <= 8) {
+    if (expect <= 4)
+      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 4, 512>), grid, block, 0, s, a);
+    else if (expect <= 8)
+      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 8, 512>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 16, 512>), grid, block, 0, s, a);
+  } else {
+    if (expect <= 4)
+      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 4, 1024>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 8, 1024>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t rank_finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_t s) {
+  const int key = (wbn ? 2 : 0) | (w_bf16 ? 1 : 0);
+  switch (key) {
+    case 0: return rank_finalize_launch<false, false>(a, s);
+    case 1: return rank_finalize_launch<false, true>(a, s);
+    case 2: return rank_finalize_launch<true, false>(a, s);
+    default: return rank_finalize_launch<true, true>(a, s);
   }
 }
 
@@ -322,6 +484,7 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
   const int t = blockIdx.x;
   const int col = (wave * kWave + lane) * kChunk;
   const bool has = col < L;
+  const uint4 gq = load16(gamma + (has ? col : L - kChunk));  // in flight across the barrier
   uint4 lq = make_uint4(0, 0, 0, 0);
   float s = 0.0f;
   if (has) {
@@ -347,7 +510,7 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
   if (has) {
     float lv[8], gv[8], out[8];
     unpack8(lq, lv);
-    unpack8(load16(gamma + col), gv);
+    unpack8(gq, gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float n = lv[e] * inv;
@@ -359,10 +522,19 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
 
 }  // namespace
 
+// With the partials asked for, the per-rank kernel writes them and (when
+// out is asked for too) a combine pass adds them in rank order; with out
+// only, the fused kernel keeps the partials on chip.
 hipError_t launch_ep_finalize(const EpArgs& a, hipStream_t s) {
   FinArgs f{a.rows, a.R, a.idx, a.R, 0, a.w, a.gamma, a.gain_center, a.eps,
-            a.b, a.K, a.P, a.tp, a.partials, a.out};
-  return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
+            a.b, a.K, a.P, a.tp, a.partials, a.out, 1};
+  if (!a.partials) return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
+  hipError_t e = rank_finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
+  if (e != hipSuccess || !a.out) return e;
+  const int64_t threads = (int64_t)a.b * (a.P / kChunk);
+  hipLaunchKernelGGL(rank_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     a.partials, a.tp, a.b, a.P, a.out);
+  return hipGetLastError();
 }
 
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
@@ -374,7 +546,7 @@ hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   FinArgs f{a.xr, 0, a.idx, a.num_rows, 1, a.w, a.gamma, a.gain_center, a.eps,
-            a.b, a.K, a.P, 1, nullptr, a.out};
+            a.b, a.K, a.P, 1, nullptr, a.out, 1};
   return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
 }
 

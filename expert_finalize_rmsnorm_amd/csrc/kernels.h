@@ -69,6 +69,9 @@ struct ProjTuning {
   int mr;             // tiles per wave unit
   int pf;             // prefetch depth
 };
+// Compute units of the current device (queried once; 256 if the query fails).
+int device_cu_count();
+
 // rows: weight rows of the grid (2I for gate/up), K: reduction length;
 // always_partials: the epilogue needs the reduction kernel even unsplit.
 ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const ProjTuning& t);

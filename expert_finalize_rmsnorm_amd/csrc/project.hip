@@ -59,8 +59,9 @@ __device__ __forceinline__ float silu(float z) {
 
 // h of one (gate, up) FP32 pair: both rounded to BF16 first.
 __device__ __forceinline__ float gated(float gate, float up) {
-  const float gs = __uint_as_float(bf16_bits(gate) << 16);
-  const float us = __uint_as_float(bf16_bits(up) << 16);
+  const uint32_t q = pack2_rn(gate, up);
+  const float gs = bf16_lo(q);
+  const float us = bf16_hi(q);
   const float a = silu(gs);
   return a * us;
 }
@@ -215,10 +216,24 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* partials
   const int64_t width = (MODE == kGateUp) ? 2 * (int64_t)N : N;
   f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   f32x4_t s1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s = 0; s < splits; ++s) {
-    const float* p = partials + ((int64_t)s * b + tok) * width;
-    s0 = s0 + *reinterpret_cast<const f32x4_t*>(p + r);
-    if (MODE == kGateUp) s1 = s1 + *reinterpret_cast<const f32x4_t*>(p + N + r);
+  // Batches of 8 slices: all loads of a batch issue before the in-order adds
+  // (indices past the last slice re-read it and are not added).
+  constexpr int kBatch = 8;
+  for (int s = 0; s < splits; s += kBatch) {
+    f32x4_t g[kBatch], u[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float* p = partials + ((int64_t)min(s + j, splits - 1) * b + tok) * width;
+      g[j] = *reinterpret_cast<const f32x4_t*>(p + r);
+      if (MODE == kGateUp) u[j] = *reinterpret_cast<const f32x4_t*>(p + N + r);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (s + j < splits) {
+        s0 = s0 + g[j];
+        if (MODE == kGateUp) s1 = s1 + u[j];
+      }
+    }
   }
   if (MODE == kLinear) {
     float o[4] = {s0[0], s0[1], s0[2], s0[3]};
@@ -244,18 +259,6 @@ int token_blocks(int b) {
 
 int round_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
 
 // The plan: `blocks` blocks (one per CU) split over `splits` K slices; each
 // slice's activations must fit the LDS (row pitch rounded to 128 + 8
@@ -274,7 +277,7 @@ constexpr Shape kShapes[] = {{1, 8, 7},  {1, 8, 8},  {1, 8, 14}, {1, 8, 16}, {2,
 ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
   const int tok = 16 * token_blocks(b);
   const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
-  const int blocks = t.target_blocks > 0 ? t.target_blocks : cu_count();
+  const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
   double best = 1e300;
   ProjPlan p{};
   for (int splits = 1; splits <= 64; splits *= 2) {
@@ -283,7 +286,7 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
     if (round_up_i(kps, 128) > kmax) continue;  // slice does not fit the LDS
     if (kps < kKStep * 4 && splits > 1) continue;
     const int real_splits = (K + kps - 1) / kps;
-    const int bps = (blocks + real_splits - 1) / real_splits;
+    const int bps = blocks / real_splits > 0 ? blocks / real_splits : 1;  // grid <= blocks
     for (const Shape& sh : kShapes) {
       if (t.waves > 0 && sh.waves != t.waves) continue;
       if (t.mr > 0 ? sh.mr != t.mr : sh.mr != 1) continue;
@@ -363,6 +366,20 @@ hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// CUs of the current device (256 on MI355X), read once.
+int device_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
 
 ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
   return make_plan(b, rows, K, always_partials, t);

@@ -87,8 +87,10 @@ extern "C" {
  *   partials      [tp][b][P] BF16 written (the resident rank-partial
  *                 buffer), or NULL when only `out` is wanted.
  *   out           [b][P] BF16 written, or NULL for partials only.
- *   At least one of partials / out must be given.  The combine happens in
- *   the same launch, so `out` never needs `partials` to be written.
+ *   At least one of partials / out must be given.  With out alone the
+ *   combine happens in the launch that forms the partials (they are never
+ *   written); with both, out is the rank-order sum of the written partials.
+ *   The results are the same bits either way.
  *   eps >= 0 and finite; gain_center finite.
  *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0,
  *   b <= 65535, rows_per_rank >= 1.

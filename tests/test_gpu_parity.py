@@ -99,6 +99,31 @@ def test_ep_ragged_and_edges(b, K, P, tp, wbn):
     finalize_bar(got_p, want_p, "partials")
     finalize_bar(got_o, want_o, "out")
     assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+    _, only_o = run_ep(inp, wbn, mode="out")  # the fused kernel
+    assert np.array_equal(only_o, want_o)
+
+
+@pytest.mark.parametrize("wbn", [True, False])
+def test_ep_skewed_ranks(wbn):
+    """Uneven route ownership: rank 0 holds 13 of 16 routes (more than one
+    batch of rows), ranks 1-3 one each, ranks 4-7 none (+0 partials)."""
+    inp = workloads.ep_finalize(11, b=6, K=16, P=3584, tp=1, outlier_frac=0.0)
+    tp = 8
+    rows1 = inp["rows"][0]
+    owner = np.array([0] * 13 + [1, 2, 3])
+    idx = np.full((tp, 6, 16), -1, np.int32)
+    for k in range(16):
+        idx[owner[k], :, k] = inp["idx"][0, :, k]
+    inp.update(rows=np.ascontiguousarray(np.broadcast_to(rows1, (tp,) + rows1.shape)), idx=idx,
+               tp=tp)
+    want_p, want_o = oracle_ep(inp, wbn)
+    assert not want_p[4:].any()
+    for mode in ("both", "partials", "out"):
+        got_p, got_o = run_ep(inp, wbn, mode=mode)
+        if got_p is not None:
+            assert np.array_equal(got_p, want_p), mode
+        if got_o is not None:
+            assert np.array_equal(got_o, want_o), mode
 
 
 def test_ep_absent_and_out_of_range_indices():

@@ -60,6 +60,7 @@ struct ProjPlan {
   int mr;            // 16-row tiles per wave unit (1 or 2)
   int pf;            // k steps in flight per wave (4 or 8)
   int blocks_per_slice;
+  int hold;          // units a wave keeps in registers until its stream ends
 };
 // Plan knobs: 0 = the library's choice.
 struct ProjTuning {

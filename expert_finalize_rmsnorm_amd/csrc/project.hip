@@ -46,7 +46,8 @@ struct FxArgs {
   int k_per_split;
   int blocks_per_slice;
   int pitch;           // LDS row pitch of the staged activations (elements)
-  float* partials;     // [splits][b][N], or null for the direct epilogue
+  f32x4_t* partials;   // [splits][N / 16][NT][64] tile-major, or null for the
+                       // direct epilogue
   const uint16_t* rs;  // direct epilogue only: [b][N] or null
   uint16_t* out;       // direct epilogue only: [b][N]
 };
@@ -78,7 +79,11 @@ __device__ __forceinline__ uint2 pack4_pz(float a, float b, float c, float d) {
 // and reused for every unit the block streams.  Each wave's (unit, k step)
 // sequence is one flat stream: the kPF-deep prefetch ring runs across unit
 // boundaries, and a unit's FP32 result leaves as soon as its last step is in.
-template <int NT, int MR, int kPF, int kWaves>
+// With kHold > 0 a wave keeps the FP32 results of its first kHold units in
+// registers and stores them after its last k step: partial stores issued in
+// the middle of the weight stream hold up the loads behind them (vector
+// memory operations complete in issue order), stores after it do not.
+template <int NT, int MR, int kPF, int kWaves, int kHold>
 __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
   extern __shared__ uint16_t xs[];  // [16 * NT][pitch]
   const int lane = threadIdx.x & (kWave - 1);
@@ -147,8 +152,45 @@ __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
   const uint16_t* xl = xs + lrow * a.pitch + 8 * kq;
   int c_unit = u, c_step = 0;
 
-  // Accumulator lane layout: rows 16 * tile + 4 * (lane / 16) + v, token lane % 16.
+  // Accumulator lane layout: rows 16 * tile + 4 * (lane / 16) + v, token
+  // 16 * nt + lane % 16.  Split partials keep exactly that layout, one 1 KB
+  // store per (tile, token block); padded tokens are stored too and never read.
+  const int ntiles = a.N / 16;
+  auto store_partial = [&](const f32x4_t (&v)[MR][NT], int unit) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        a.partials[(((int64_t)slice * ntiles + unit * MR + m) * NT + nt) * kWave + lane] = v[m][nt];
+  };
+  f32x4_t hold[kHold > 0 ? kHold : 1][MR][NT];
+  int held = 0;
   auto emit = [&]() {
+    if (a.partials) {
+      f32x4_t v[MR][NT];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          v[m][nt] = acc[m][nt];
+          acc[m][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      if (kHold > 0 && held < kHold) {
+        // wave-uniform slot: register moves, no memory operation
+#pragma unroll
+        for (int j = 0; j < (kHold > 0 ? kHold : 1); ++j)
+          if (j == held) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) hold[j][m][nt] = v[m][nt];
+          }
+        ++held;
+      } else {
+        store_partial(v, c_unit);
+      }
+      return;
+    }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       const int r = (c_unit * MR + m) * 16 + 4 * kq;
@@ -158,20 +200,16 @@ __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
         const f32x4_t s = acc[m][nt];
         acc[m][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         if (tok >= a.b) continue;
-        if (a.partials) {
-          *reinterpret_cast<f32x4_t*>(a.partials + ((int64_t)slice * a.b + tok) * a.N + r) = s;
-        } else {
-          float o[4] = {s[0], s[1], s[2], s[3]};
-          if (a.rs) {
-            const uint2 q2 = *reinterpret_cast<const uint2*>(a.rs + (int64_t)tok * a.N + r);
-            o[0] = o[0] + bf16_lo(q2.x);
-            o[1] = o[1] + bf16_hi(q2.x);
-            o[2] = o[2] + bf16_lo(q2.y);
-            o[3] = o[3] + bf16_hi(q2.y);
-          }
-          *reinterpret_cast<uint2*>(a.out + (int64_t)tok * a.N + r) =
-              pack4_pz(o[0], o[1], o[2], o[3]);
+        float o[4] = {s[0], s[1], s[2], s[3]};
+        if (a.rs) {
+          const uint2 q2 = *reinterpret_cast<const uint2*>(a.rs + (int64_t)tok * a.N + r);
+          o[0] = o[0] + bf16_lo(q2.x);
+          o[1] = o[1] + bf16_hi(q2.x);
+          o[2] = o[2] + bf16_lo(q2.y);
+          o[3] = o[3] + bf16_hi(q2.y);
         }
+        *reinterpret_cast<uint2*>(a.out + (int64_t)tok * a.N + r) =
+            pack4_pz(o[0], o[1], o[2], o[3]);
       }
     }
   };
@@ -199,21 +237,35 @@ __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
       next_load(ra[i]);
     }
   }
+  if (kHold > 0) {
+#pragma unroll
+    for (int j = 0; j < (kHold > 0 ? kHold : 1); ++j)
+      if (j < held) store_partial(hold[j], u + j * stride);
+  }
 }
 
-// Slice partials added in slice order, then the epilogue: one thread per 4
-// output rows of a token.  kGateUp: partials hold gate rows [0, N) and up
-// rows [N, 2N); out is h [b][N].
+// Slice partials added in slice order, then the epilogue: one thread per
+// accumulator lane of a (tile, token block), i.e. 4 output rows of one
+// token, reading the tile-major partials with 1 KB per wave and slice.
+// kGateUp: partial tiles [0, N/16) are gate rows, [N/16, N/8) up rows; out
+// is h [b][N].
 template <int MODE>
-__global__ void __launch_bounds__(256) split_reduce_kernel(const float* partials, int splits, int b,
-                                                          int N, const uint16_t* rs,
-                                                          uint16_t* out) {
-  const int quads = N / 4;
+__global__ void __launch_bounds__(256) split_reduce_kernel(const f32x4_t* partials, int splits,
+                                                          int b, int nt_blocks, int N,
+                                                          const uint16_t* rs, uint16_t* out) {
+  const int out_tiles = N / 16;
+  const int64_t per_tile = (int64_t)nt_blocks * kWave;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)b * quads) return;
-  const int tok = (int)(i / quads);
-  const int r = (int)(i - (int64_t)tok * quads) * 4;
-  const int64_t width = (MODE == kGateUp) ? 2 * (int64_t)N : N;
+  if (i >= out_tiles * per_tile) return;
+  const int tile = (int)(i / per_tile);
+  const int rem = (int)(i - tile * per_tile);
+  const int lane = rem & (kWave - 1);
+  const int tok = 16 * (rem / kWave) + (lane & 15);
+  if (tok >= b) return;
+  const int r = tile * 16 + 4 * (lane >> 4);
+  const int tiles_in = (MODE == kGateUp) ? 2 * out_tiles : out_tiles;
+  const int64_t slice_stride = (int64_t)tiles_in * per_tile;
+  const int64_t up_off = (int64_t)out_tiles * per_tile;
   f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   f32x4_t s1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // Batches of 8 slices: all loads of a batch issue before the in-order adds
@@ -223,9 +275,9 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const float* partials
     f32x4_t g[kBatch], u[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      const float* p = partials + ((int64_t)min(s + j, splits - 1) * b + tok) * width;
-      g[j] = *reinterpret_cast<const f32x4_t*>(p + r);
-      if (MODE == kGateUp) u[j] = *reinterpret_cast<const f32x4_t*>(p + N + r);
+      const f32x4_t* p = partials + (int64_t)min(s + j, splits - 1) * slice_stride + i;
+      g[j] = p[0];
+      if (MODE == kGateUp) u[j] = p[up_off];
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -301,7 +353,7 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
       const double x_bytes = (double)blocks * tok * kps * 2.0;
       // partials written and re-read, plus the reduction launch (~4 us)
       const double p_bytes = (real_splits > 1 || always_partials)
-                                 ? real_splits * (double)b * rows * 4.0 * 2.0 + 16.0e6 : 0.0;
+                                 ? real_splits * (double)tok * rows * 4.0 * 2.0 + 16.0e6 : 0.0;
       const double cost = a_bytes + x_bytes + p_bytes;
       if (cost < best * 0.999) {
         best = cost;
@@ -313,6 +365,9 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
         p.mr = sh.mr;
         p.pf = sh.pf;
         p.blocks_per_slice = bps;
+        // Results held until the stream ends: up to 4 units of one tile and
+        // at most 4 token blocks, at most 2 waves per SIMD (256 VGPRs a lane).
+        p.hold = (sh.mr == 1 && tok <= 64 && w <= 8 && per_wave <= 4) ? 4 : 0;
       }
     }
   }
@@ -324,16 +379,16 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   return p;  // splits == 0: no slice of K fits the LDS
 }
 
-template <int NT, int MR, int PF, int W>
+template <int NT, int MR, int PF, int W, int H>
 hipError_t px_launch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   static bool attr_set = false;  // idempotent: every call sets the same maximum
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_kernel<NT, MR, PF, W>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_kernel<NT, MR, PF, W, H>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((px_kernel<NT, MR, PF, W>), dim3(p.splits * p.blocks_per_slice),
+  hipLaunchKernelGGL((px_kernel<NT, MR, PF, W, H>), dim3(p.splits * p.blocks_per_slice),
                      dim3(kWave * W), p.lds, s, a);
   return hipGetLastError();
 }
@@ -341,14 +396,28 @@ hipError_t px_launch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
 template <int MR, int PF, int W>
 hipError_t px_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   switch (token_blocks(a.b)) {
-    case 1: return px_launch<1, MR, PF, W>(a, p, s);
-    case 2: return px_launch<2, MR, PF, W>(a, p, s);
-    case 4: return px_launch<4, MR, PF, W>(a, p, s);
-    default: return px_launch<8, MR, PF, W>(a, p, s);
+    case 1: return px_launch<1, MR, PF, W, 0>(a, p, s);
+    case 2: return px_launch<2, MR, PF, W, 0>(a, p, s);
+    case 4: return px_launch<4, MR, PF, W, 0>(a, p, s);
+    default: return px_launch<8, MR, PF, W, 0>(a, p, s);
+  }
+}
+
+template <int W>
+hipError_t px_dispatch_hold(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  switch (token_blocks(a.b)) {
+    case 1: return px_launch<1, 1, 8, W, 4>(a, p, s);
+    case 2: return px_launch<2, 1, 8, W, 4>(a, p, s);
+    case 4: return px_launch<4, 1, 8, W, 4>(a, p, s);
+    default: return hipErrorInvalidValue;  // not planned (more than 4 token blocks)
   }
 }
 
 hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (p.hold && a.partials) {
+    if (p.mr != 1 || p.pf != 8 || p.waves > 8 || token_blocks(a.b) > 4) return hipErrorInvalidValue;
+    return p.waves == 7 ? px_dispatch_hold<7>(a, p, s) : px_dispatch_hold<8>(a, p, s);
+  }
   const int key = p.mr * 1000 + p.pf * 100 + p.waves;
   switch (key) {
     case 1807: return px_dispatch_nt<1, 8, 7>(a, p, s);
@@ -386,20 +455,23 @@ ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const Pro
 }
 
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
-  return (p.splits > 1 || always) ? sizeof(float) * (size_t)p.splits * b * n_out : 0;
+  const size_t tok = 16 * (size_t)token_blocks(b);  // padded tokens are stored too
+  return (p.splits > 1 || always) ? sizeof(float) * (size_t)p.splits * tok * n_out : 0;
 }
 
 hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X, int b,
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
   const bool split = plan.splits > 1;
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
-           split ? partials : nullptr, rs, out};
+           split ? part : nullptr, rs, out};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess || !split) return e;
-  const int64_t threads = (int64_t)b * (N / 4);
+  const int ntb = token_blocks(b);
+  const int64_t threads = (int64_t)(N / 16) * ntb * kWave;
   hipLaunchKernelGGL(split_reduce_kernel<kLinear>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     0, s, partials, plan.splits, b, N, rs, out);
+                     0, s, part, plan.splits, b, ntb, N, rs, out);
   return hipGetLastError();
 }
 
@@ -407,13 +479,15 @@ hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int I, int H, 
                           int b, uint16_t* h, const ProjPlan& plan, float* partials,
                           hipStream_t s) {
   // Gate rows [0, I) and up rows [I, 2I) in one grid; SiLU in the reduction.
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{Wg, Wu, I, 2 * I, H, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
-           partials, nullptr, nullptr};
+           part, nullptr, nullptr};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess) return e;
-  const int64_t threads = (int64_t)b * (I / 4);
+  const int ntb = token_blocks(b);
+  const int64_t threads = (int64_t)(I / 16) * ntb * kWave;
   hipLaunchKernelGGL(split_reduce_kernel<kGateUp>, dim3((unsigned)((threads + 255) / 256)),
-                     dim3(256), 0, s, partials, plan.splits, b, I, nullptr, h);
+                     dim3(256), 0, s, part, plan.splits, b, ntb, I, nullptr, h);
   return hipGetLastError();
 }
 

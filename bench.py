@@ -12,7 +12,8 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
   3. the rank-order combine of the 8 partials, RMSNorm, and the 3584 -> 7168
      up projection plus rs -> out [64, 7168] (moetail_combine_norm_upproj).
 
-Each step replays a HIP graph of the three calls in order on one stream
+Steps replay HIP graphs of the three calls in order on one stream, two steps
+(one per input set) per graph
 (--streams 2 puts the finalize on a side stream beside the shared expert:
 measured slower, the cross-stream fork and join inside the graph cost more
 than the overlap gains); two input sets (weights and rows) alternate so that the 315 MB of weights per step stream from HBM,
@@ -36,6 +37,26 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
 
 
+# HBM bytes of one moetail_shared_expert call at b=64 (its four kernels), from
+# two rocprofv3 --pmc passes over `bench.py --steps 3 --warmup 1
+# --no-cpu-baseline --no-kernels --copy-calibration`: FETCH_SIZE and WRITE_SIZE
+# per dispatch, scaled by what each reads for the calibration kernel (256 MiB
+# in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the
+# kernel sources with this digest only.
+TRAFFIC = dict(source_digest="0b0997c8e4fe5b0b", fetch_bytes=310882 * 1024,
+               write_bytes=40576 * 1024)
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "expert_finalize_rmsnorm_amd", "csrc")
+    for name in ("common.h", "kernels.h", "project.hip", "api.hip", "finalize.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -56,6 +77,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-config kernel table")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with two launches of a plain elementwise kernel over 256 MiB "
+                         "(reads 256 MiB, writes 256 MiB): the scale for HBM byte counters")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the finalize on a side stream beside the shared expert; "
                          "1: the three calls in order on one stream")
@@ -128,24 +152,31 @@ def main():
     for d in sets:
         step(d)  # eager once before capture
     torch.cuda.synchronize()
+    # One graph holds a step on each input set (two steps per replay: a
+    # decode loop captures many layers' tails in one graph, so the boundary
+    # between replays is shared); an odd step count ends with a one-step graph.
     cap = torch.cuda.Stream()
-    graphs = []
-    for d in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
+    pair, single = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(pair, stream=cap):
+        for d in sets:
             step(d)
-        graphs.append(g)
+    with torch.cuda.graph(single, stream=cap):
+        step(sets[0])
     torch.cuda.synchronize()
 
+    def run_steps(n):
+        for _ in range(n // nsets):
+            pair.replay()
+        if n % nsets:
+            single.replay()
+
     log(f"warmup {args.warmup}, timed {args.steps} steps")
-    for i in range(args.warmup):
-        graphs[i % nsets].replay()
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        graphs[i % nsets].replay()
+    run_steps(args.steps)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -170,14 +201,31 @@ def main():
                      frac=round(algo[n] / per_call[n] / 1e3 / HBM_PEAK_GBPS, 4))
              for n in per_call}
     dom = "shared_expert"
-    roofline = dict(bound="hbm", kernel="moetail_shared_expert (gate/up + down), b=64",
+    traffic = traffic_bytes = None
+    if kernel_source_digest() == TRAFFIC["source_digest"]:
+        traffic_bytes = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+        traffic = round(traffic_bytes / per_call[dom] / 1e3, 1)
+    roofline = dict(bound="hbm",
+                    kernel="moetail_shared_expert at b=64: gate/up and down projections with "
+                           "their split reductions (4 kernels, one call)",
                     achieved=entry[dom]["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
-                    frac=entry[dom]["frac"], traffic=None)
+                    frac=entry[dom]["frac"], traffic=traffic, traffic_bytes=traffic_bytes,
+                    algorithmic_bytes=algo[dom])
 
     kernels = None
     if not args.no_kernels:
         log("per-config kernel timings")
         kernels = config_kernels(sets[0], log)
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("copy calibration: 2 x neg over 268435456 B in, 268435456 B out")
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -12,7 +12,10 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
   3. the rank-order combine of the 8 partials, RMSNorm, and the 3584 -> 7168
      up projection plus rs -> out [64, 7168] (moetail_combine_norm_upproj).
 
-Steps replay HIP graphs of the three calls in order on one stream, two steps
+Steps 2 and 3 run as one moetail_tail call (five launches; --tail calls runs
+them as their two entry points, eight launches: the same bits).
+
+Steps replay HIP graphs of the calls in order on one stream, two steps
 (one per input set) per graph
 (--streams 2 puts the finalize on a side stream beside the shared expert:
 measured slower, the cross-stream fork and join inside the graph cost more
@@ -67,7 +70,8 @@ def algorithmic_bytes():
     fin = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2 + TP * B * P * 2
     shared = 3 * H * I * 2 + B * H * 2 + B * H * 2
     upproj = TP * B * P * 2 + P * 2 + H * P * 2 + B * H * 2 + B * H * 2
-    return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj)
+    return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj,
+                tail=shared + upproj - B * H * 2 * 2)
 
 
 def main():
@@ -80,6 +84,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with two launches of a plain elementwise kernel over 256 MiB "
                          "(reads 256 MiB, writes 256 MiB): the scale for HBM byte counters")
+    ap.add_argument("--tail", choices=("fused", "calls"), default="fused",
+                    help="fused: the shared expert and combine+norm+upproj as one "
+                         "moetail_tail call; calls: as its two entry points")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the finalize on a side stream beside the shared expert; "
                          "1: the three calls in order on one stream")
@@ -112,6 +119,7 @@ def main():
                  out=torch.empty((B, H), dtype=torch.int16, device="cuda"),
                  ws_sh=mt.new_workspace(mt.OP_SHARED_EXPERT, B, H, I),
                  ws_up=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, B, P, H, TP),
+                 ws_tail=mt.new_workspace(mt.OP_TAIL, B, P, H, I),
                  host=(ep, up, sh) if s == 0 else None)
         sets.append(d)
     torch.cuda.synchronize()
@@ -127,11 +135,19 @@ def main():
         mt.moetail_combine_norm_upproj(d["lat"], d["lgamma"], 1e-6, d["w_up"], d["out"],
                                        rs=d["rs"], workspace=d["ws_up"])
 
+    def tail(d):
+        mt.moetail_tail(d["lat"], d["lgamma"], 1e-6, d["w_up"], d["x"], d["wg"], d["wu"], d["wd"],
+                        d["out"], rs=d["rs"], workspace=d["ws_tail"])
+
     side = torch.cuda.Stream()
 
     def step(d):
         """finalize runs on a side stream beside the shared expert; the up
         projection waits for both (a fork/join inside the captured graph)."""
+        if args.tail == "fused":
+            finalize(d)
+            tail(d)
+            return
         if args.streams == 1:
             finalize(d)
             shared(d)
@@ -183,7 +199,8 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = B / (ms_per_step * 1e-3)
-    step_bytes = sum(algorithmic_bytes().values())
+    algo0 = algorithmic_bytes()
+    step_bytes = algo0["finalize"] + algo0["shared_expert"] + algo0["combine_norm_upproj"]
     log(f"step {ms_per_step * 1e3:.1f} us wall, {gpu_ms * 1e3:.1f} us GPU events")
 
     # Per entry point: a HIP graph of back-to-back calls (rotating the input
@@ -194,7 +211,7 @@ def main():
 
     per_call = {n: time_calls(f) for n, f in
                 (("finalize", finalize), ("shared_expert", shared),
-                 ("combine_norm_upproj", upproj))}
+                 ("combine_norm_upproj", upproj), ("tail", tail))}
     algo = algorithmic_bytes()
     entry = {n: dict(us=round(per_call[n], 2), bytes=algo[n],
                      GBps=round(algo[n] / per_call[n] / 1e3, 1),
@@ -249,7 +266,7 @@ def main():
                                "expert 7168x6144 SiLU -> latent combine + RMSNorm + up "
                                "projection 3584->7168 (+rs)",
                    "b": B, "P": P, "tp": TP, "K": K, "H": H, "I": I,
-                   "global_batch": B, "streams": args.streams,
+                   "global_batch": B, "tail": args.tail, "streams": args.streams,
                    "parallelism": "one GPU, tp rank partials resident"},
         "gpu_ms_per_step_events": round(gpu_ms, 5),
         "step_algorithmic_bytes": step_bytes,

@@ -22,10 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libmoetail.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
-OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT = 0, 1, 2, 3
+OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL = 0, 1, 2, 3, 4
 
-ENTRY_POINTS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-                "moetail_shared_expert", "moetail_workspace_bytes", "moetail_status_string")
+_CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
+          "moetail_shared_expert", "moetail_tail")
+ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string")
 
 
 class MoetailError(RuntimeError):
@@ -54,11 +55,13 @@ def lib() -> ctypes.CDLL:
         L.moetail_combine_norm_upproj.argtypes = [P, I32, P, F, P, I32, P, I32, I32, P, P, P,
                                                   SZ, P]
         L.moetail_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, SZ, P]
+        L.moetail_tail.argtypes = [P, I32, P, F, P, I32, P, P, P, P, I32, I32, I32, P, P, P, P,
+                                   P, SZ, P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
         L.moetail_status_string.restype = ctypes.c_char_p
-        for f in ENTRY_POINTS[:4]:
+        for f in _CALLS:
             getattr(L, f).restype = I32
         _lib = L
     return _lib
@@ -176,6 +179,30 @@ def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, s
     st = lib().moetail_shared_expert(_ptr(x), b, H, _ptr(w_gate), _ptr(w_up), I, _ptr(w_down),
                                      _ptr(h), _ptr(rs), ws, wsb, _stream(stream))
     _check(st, "moetail_shared_expert")
+
+
+def moetail_tail(latent_partials, gamma, eps, w_up, x, w_gate, w_up_shared, w_down, out,
+                 rs=None, normed=None, h=None, workspace=None, stream=None):
+    """The tail after the finalize in one call: rs = shared expert of x,
+    out = up projection of the normed rank-combined latent + rs.
+    latent_partials [tp, b, L], gamma [L], w_up [H, L]; x [b, H], w_gate and
+    w_up_shared [I, H], w_down [H, I]; writes out [b, H] and rs [b, H],
+    normed [b, L], h [b, I] when given.  workspace: at least
+    workspace_bytes(OP_TAIL, b, L, H, I) bytes."""
+    for t, n in ((latent_partials, "latent_partials"), (gamma, "gamma"), (w_up, "w_up"),
+                 (x, "x"), (w_gate, "w_gate"), (w_up_shared, "w_up_shared"), (w_down, "w_down"),
+                 (out, "out"), (rs, "rs"), (normed, "normed"), (h, "h")):
+        _bf16(t, n)
+    tp, b, L = latent_partials.shape
+    H = x.shape[1]
+    I = w_gate.shape[0]
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moetail_tail(_ptr(latent_partials), tp, _ptr(gamma), float(eps), _ptr(w_up), L,
+                            _ptr(x), _ptr(w_gate), _ptr(w_up_shared), _ptr(w_down), H, I, b,
+                            _ptr(out), _ptr(rs), _ptr(normed), _ptr(h), ws, wsb,
+                            _stream(stream))
+    _check(st, "moetail_tail")
 
 
 def new_workspace(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0, device="cuda"):

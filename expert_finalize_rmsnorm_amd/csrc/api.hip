@@ -83,6 +83,32 @@ SharedLayout shared_layout(int b, int H, int I) {
   return l;
 }
 
+struct TailLayout {
+  ProjPlan gate_up, down, up;
+  GroupPlan group;
+  size_t h_bytes, y_bytes, down_part_bytes, part_bytes;
+};
+// The gate/up, down and up projections keep the plans of their own entry
+// points (so the sums are the same bits); down and up always go through
+// partials, since the last launch forms rs and then out.
+TailLayout tail_layout(int b, int L, int H, int I) {
+  TailLayout l;
+  l.gate_up = plan_projection(b, 2 * I, H, true, tuning("GATEUP"));
+  l.down = plan_projection(b, H, I, false, tuning("DOWN"));
+  l.up = plan_projection(b, H, L, false, tuning("UPPROJ"));
+  l.group = (l.down.splits && l.up.splits) ? plan_group(b, l.down, H, l.up, H) : GroupPlan{};
+  l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
+  l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
+  const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I, true);
+  l.down_part_bytes = round_up(proj_partial_bytes(l.down, b, H, true), 256);
+  const size_t du = l.down_part_bytes + proj_partial_bytes(l.up, b, H, true);
+  l.part_bytes = round_up(g > du ? g : du, 256);
+  return l;
+}
+bool tail_ok(const TailLayout& l) {
+  return l.gate_up.splits && l.down.splits && l.up.splits && l.group.waves;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,6 +199,42 @@ int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gat
   return hip_status(e);
 }
 
+int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
+                 const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
+                 const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
+                 uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  if (b < 0 || tp <= 0 || L <= 0 || H <= 0 || I <= 0) return MOETAIL_EINVAL;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
+  if (!a16(latent_partials) || !a16(gamma) || !a16(w_up) || !a16(x) || !a16(w_gate) ||
+      !a16(w_upw) || !a16(w_down) || !a16(out))
+    return MOETAIL_EINVAL;
+  if ((rs && !a16(rs)) || (normed && !a16(normed)) || (h && !a16(h))) return MOETAIL_EINVAL;
+  if (L % 32 || L > MOETAIL_MAX_WIDTH || H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K ||
+      I > MOETAIL_MAX_GEMM_K || tp > MOETAIL_MAX_TP || b > MOETAIL_MAX_GEMM_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
+  const TailLayout lay = tail_layout(b, L, H, I);
+  if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
+  const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
+    return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hb = h;
+  if (!hb) {
+    hb = reinterpret_cast<uint16_t*>(ws);
+    ws += lay.h_bytes;
+  }
+  uint16_t* yb = normed;
+  if (!yb) {
+    yb = reinterpret_cast<uint16_t*>(ws);
+    ws += lay.y_bytes;
+  }
+  TailArgs a{x, w_gate, w_upw, w_down, H, I, latent_partials, tp, gamma, eps, w_up, L, b, hb, yb,
+             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes};
+  return hip_status(launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream));
+}
+
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
   if (op == MOETAIL_OP_TP_FINALIZE) {
     if (b <= 0 || b > MOETAIL_MAX_TOKENS || dim0 <= 0 || dim0 > MOETAIL_MAX_ROUTES || dim1 <= 0 ||
@@ -187,6 +249,13 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
       (void)dim2;
       const UpprojLayout l = upproj_layout(b, dim0, dim1);
       return l.plan.splits ? l.y_bytes + l.part_bytes : 0;
+    }
+    case MOETAIL_OP_TAIL: {
+      if (dim0 <= 0 || dim1 <= 0 || dim2 <= 0 || dim0 % 32 || dim0 > MOETAIL_MAX_WIDTH ||
+          dim1 % 64 || dim2 % 64 || dim1 > MOETAIL_MAX_GEMM_K || dim2 > MOETAIL_MAX_GEMM_K)
+        return 0;
+      const TailLayout l = tail_layout(b, dim0, dim1, dim2);
+      return tail_ok(l) ? l.h_bytes + l.y_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_SHARED_EXPERT: {
       if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64 || dim0 > MOETAIL_MAX_GEMM_K ||

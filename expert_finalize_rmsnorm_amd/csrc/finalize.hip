@@ -23,6 +23,7 @@
 // instruction reading 1 KB of one row contiguously.
 #include "common.h"
 #include "kernels.h"
+#include "norm_device.h"
 
 namespace moetail {
 
@@ -470,54 +471,12 @@ __global__ void __launch_bounds__(256) tp_rank_sum_kernel(const uint16_t* kpart,
 
 // ------------------------------------------------------ latent combine ---
 //
-// One block per token, one wave per 512-column block: the tp latent
-// partials are added in rank order from 0 and rounded to BF16 (l), the
-// sum of squares of l is taken in the tree above, and
-// y = bf16((l * inv) * fp32(gamma)) with -0 as +0.
+// One block per token (latent_norm_body in norm_device.h).
 __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, int tp, int b,
                                                            int L, const uint16_t* gamma,
                                                            float eps, uint16_t* y) {
   __shared__ float block_ss[16];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
-  const int t = blockIdx.x;
-  const int col = (wave * kWave + lane) * kChunk;
-  const bool has = col < L;
-  const uint4 gq = load16(gamma + (has ? col : L - kChunk));  // in flight across the barrier
-  uint4 lq = make_uint4(0, 0, 0, 0);
-  float s = 0.0f;
-  if (has) {
-    float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 8
-    for (int r = 0; r < tp; ++r) {
-      float v[8];
-      unpack8(load16(lat + ((int64_t)r * b + t) * L + col), v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
-    }
-    lq = pack8(sum);
-    float lv[8];
-    unpack8(lq, lv);
-    s = chunk_sum_of_squares(lv);
-  }
-  s = wave_butterfly_sum(s);
-  if (lane == 0) block_ss[wave] = s;
-  __syncthreads();
-  float total = 0.0f;
-  for (int j = 0; j < nwaves; ++j) total = total + block_ss[j];
-  const float inv = inv_rms(total, (float)(1.0 / (double)L), eps);
-  if (has) {
-    float lv[8], gv[8], out[8];
-    unpack8(lq, lv);
-    unpack8(gq, gv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float n = lv[e] * inv;
-      out[e] = n * gv[e];
-    }
-    store16(y + (int64_t)t * L + col, pack8_pz(out));
-  }
+  latent_norm_body(lat, tp, b, L, gamma, eps, y, blockIdx.x, block_ss);
 }
 
 }  // namespace

@@ -79,6 +79,38 @@ ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const Pro
 // FP32 partial bytes of a plan (always: also for a single slice).
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always);
 
+// Two projections in one grid: blocks_per_slice of each (keeping each
+// plan's K slices), the common waves per block and units held per wave.
+struct GroupPlan {
+  int bps0, bps1;
+  int waves;
+  int hold;
+};
+GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1);
+
+// The fused tail (moetail_tail): gate/up -> {h, y} -> {down, up} -> {rs, out}.
+struct TailArgs {
+  const uint16_t* x;        // [b][H]
+  const uint16_t* w_gate;   // [I][H]
+  const uint16_t* w_upw;    // [I][H]
+  const uint16_t* w_down;   // [H][I]
+  int H, I;
+  const uint16_t* lat;      // [tp][b][L]
+  int tp;
+  const uint16_t* gamma;    // [L]
+  float eps;
+  const uint16_t* w_up;     // [H][L]
+  int L, b;
+  uint16_t* h;              // [b][I] (caller's or workspace)
+  uint16_t* y;              // [b][L] (caller's or workspace)
+  uint16_t* rs;             // [b][H] or null
+  uint16_t* out;            // [b][H]
+  float* partials;          // gate/up partials, then down and up partials
+  size_t down_part_bytes;   // offset of the up partials
+};
+hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
+                       const ProjPlan& up, const GroupPlan& g, hipStream_t stream);
+
 // out[b][N] = bf16(W[N][K] . X[b][K] + rs), -0 as +0.
 hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X,
                          int b, const uint16_t* rs, uint16_t* out,

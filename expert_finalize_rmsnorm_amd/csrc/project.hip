@@ -24,6 +24,7 @@
 // in-order MFMA chain.
 #include "common.h"
 #include "kernels.h"
+#include "norm_device.h"
 
 namespace moetail {
 
@@ -84,19 +85,19 @@ __device__ __forceinline__ uint2 pack4_pz(float a, float b, float c, float d) {
 // the middle of the weight stream hold up the loads behind them (vector
 // memory operations complete in issue order), stores after it do not.
 template <int NT, int MR, int kPF, int kWaves, int kHold>
-__global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
+__device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   extern __shared__ uint16_t xs[];  // [16 * NT][pitch]
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15;
   const int kq = lane >> 4;
   const int K = a.K;
-  const int slice = blockIdx.x / a.blocks_per_slice;
+  const int slice = block / a.blocks_per_slice;
   const int kb = slice * a.k_per_split;
   const int ke = min(K, kb + a.k_per_split);
   const int nsteps = (ke - kb) / kKStep;
   const int stride = a.blocks_per_slice * kWaves;
-  const int u = (blockIdx.x - slice * a.blocks_per_slice) * kWaves + wave;
+  const int u = (block - slice * a.blocks_per_slice) * kWaves + wave;
   const int nunits = a.N / (16 * MR);
   const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // wave-uniform
   const int total = my_units * nsteps;
@@ -244,32 +245,38 @@ __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
   }
 }
 
+template <int NT, int MR, int kPF, int kWaves, int kHold>
+__global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
+  px_body<NT, MR, kPF, kWaves, kHold>(a, blockIdx.x);
+}
+
+// Two independent projections in one persistent grid (the fused tail's down
+// and up projections): blocks [0, blocks0) run a0's plan, the rest a1's.
+template <int NT, int kWaves, int kHold>
+__global__ void __launch_bounds__(kWave * kWaves) px_group_kernel(FxArgs a0, FxArgs a1,
+                                                                  int blocks0) {
+  if ((int)blockIdx.x < blocks0)
+    px_body<NT, 1, 8, kWaves, kHold>(a0, blockIdx.x);
+  else
+    px_body<NT, 1, 8, kWaves, kHold>(a1, blockIdx.x - blocks0);
+}
+
 // Slice partials added in slice order, then the epilogue: one thread per
 // accumulator lane of a (tile, token block), i.e. 4 output rows of one
 // token, reading the tile-major partials with 1 KB per wave and slice.
 // kGateUp: partial tiles [0, N/16) are gate rows, [N/16, N/8) up rows; out
 // is h [b][N].
+
+// Sum over the splits of element i of each slice (slice_stride apart), in
+// slice order from +0; with kGateUp also of element i + up_off.  Batches of
+// 8 slices: all loads of a batch issue before the in-order adds (indices
+// past the last slice re-read it and are not added).
 template <int MODE>
-__global__ void __launch_bounds__(256) split_reduce_kernel(const f32x4_t* partials, int splits,
-                                                          int b, int nt_blocks, int N,
-                                                          const uint16_t* rs, uint16_t* out) {
-  const int out_tiles = N / 16;
-  const int64_t per_tile = (int64_t)nt_blocks * kWave;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= out_tiles * per_tile) return;
-  const int tile = (int)(i / per_tile);
-  const int rem = (int)(i - tile * per_tile);
-  const int lane = rem & (kWave - 1);
-  const int tok = 16 * (rem / kWave) + (lane & 15);
-  if (tok >= b) return;
-  const int r = tile * 16 + 4 * (lane >> 4);
-  const int tiles_in = (MODE == kGateUp) ? 2 * out_tiles : out_tiles;
-  const int64_t slice_stride = (int64_t)tiles_in * per_tile;
-  const int64_t up_off = (int64_t)out_tiles * per_tile;
-  f32x4_t s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4_t s1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  // Batches of 8 slices: all loads of a batch issue before the in-order adds
-  // (indices past the last slice re-read it and are not added).
+__device__ __forceinline__ void slice_sum(const f32x4_t* partials, int splits,
+                                          int64_t slice_stride, int64_t i, int64_t up_off,
+                                          f32x4_t& s0, f32x4_t& s1) {
+  s0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  s1 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int kBatch = 8;
   for (int s = 0; s < splits; s += kBatch) {
     f32x4_t g[kBatch], u[kBatch];
@@ -287,21 +294,97 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(const f32x4_t* partia
       }
     }
   }
+}
+
+// Element i's token and first output row; false for padded tokens.
+__device__ __forceinline__ bool lane_position(int64_t i, int64_t per_tile, int b, int& tok,
+                                              int& r) {
+  const int tile = (int)(i / per_tile);
+  const int rem = (int)(i - tile * per_tile);
+  const int lane = rem & (kWave - 1);
+  tok = 16 * (rem / kWave) + (lane & 15);
+  r = tile * 16 + 4 * (lane >> 4);
+  return tok < b;
+}
+
+__device__ __forceinline__ void add_bf16x4(float (&o)[4], uint2 q2) {
+  o[0] = o[0] + bf16_lo(q2.x);
+  o[1] = o[1] + bf16_hi(q2.x);
+  o[2] = o[2] + bf16_lo(q2.y);
+  o[3] = o[3] + bf16_hi(q2.y);
+}
+
+template <int MODE>
+__device__ __forceinline__ void reduce_body(int64_t i, const f32x4_t* partials, int splits, int b,
+                                            int nt_blocks, int N, const uint16_t* rs,
+                                            uint16_t* out) {
+  const int out_tiles = N / 16;
+  const int64_t per_tile = (int64_t)nt_blocks * kWave;
+  if (i >= out_tiles * per_tile) return;
+  int tok, r;
+  if (!lane_position(i, per_tile, b, tok, r)) return;
+  const int tiles_in = (MODE == kGateUp) ? 2 * out_tiles : out_tiles;
+  f32x4_t s0, s1;
+  slice_sum<MODE>(partials, splits, (int64_t)tiles_in * per_tile, i,
+                  (int64_t)out_tiles * per_tile, s0, s1);
   if (MODE == kLinear) {
     float o[4] = {s0[0], s0[1], s0[2], s0[3]};
-    if (rs) {
-      const uint2 q2 = *reinterpret_cast<const uint2*>(rs + (int64_t)tok * N + r);
-      o[0] = o[0] + bf16_lo(q2.x);
-      o[1] = o[1] + bf16_hi(q2.x);
-      o[2] = o[2] + bf16_lo(q2.y);
-      o[3] = o[3] + bf16_hi(q2.y);
-    }
+    if (rs) add_bf16x4(o, *reinterpret_cast<const uint2*>(rs + (int64_t)tok * N + r));
     *reinterpret_cast<uint2*>(out + (int64_t)tok * N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
   } else {
     *reinterpret_cast<uint2*>(out + (int64_t)tok * N + r) =
         pack4_pz(gated(s0[0], s1[0]), gated(s0[1], s1[1]), gated(s0[2], s1[2]),
                  gated(s0[3], s1[3]));
   }
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256) split_reduce_kernel(const f32x4_t* partials, int splits,
+                                                          int b, int nt_blocks, int N,
+                                                          const uint16_t* rs, uint16_t* out) {
+  reduce_body<MODE>((int64_t)blockIdx.x * blockDim.x + threadIdx.x, partials, splits, b,
+                    nt_blocks, N, rs, out);
+}
+
+// The fused tail's middle launch: blocks [0, red_blocks) form h from the
+// gate/up partials (as split_reduce_kernel<kGateUp>); each later block is
+// one token's latent combine + RMSNorm (as latent_norm_kernel).  The two
+// parts share no data.
+__global__ void __launch_bounds__(1024) tail_mid_kernel(const f32x4_t* gu_partials, int gu_splits,
+                                                        int b, int nt_blocks, int I, uint16_t* h,
+                                                        int red_blocks, const uint16_t* lat,
+                                                        int tp, int L, const uint16_t* gamma,
+                                                        float eps, uint16_t* y) {
+  __shared__ float block_ss[16];
+  if ((int)blockIdx.x < red_blocks) {
+    reduce_body<kGateUp>((int64_t)blockIdx.x * blockDim.x + threadIdx.x, gu_partials, gu_splits,
+                         b, nt_blocks, I, nullptr, h);
+    return;
+  }
+  latent_norm_body(lat, tp, b, L, gamma, eps, y, blockIdx.x - red_blocks, block_ss);
+}
+
+// The fused tail's last launch: rs = bf16(sum of the down partials), then
+// out = bf16(sum of the up-projection partials + rs), -0 as +0 both times
+// (the values moetail_shared_expert and moetail_combine_norm_upproj give).
+__global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_partials,
+                                                      int down_splits, const f32x4_t* up_partials,
+                                                      int up_splits, int b, int nt_blocks, int N,
+                                                      uint16_t* rs, uint16_t* out) {
+  const int64_t per_tile = (int64_t)nt_blocks * kWave;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (N / 16) * per_tile) return;
+  int tok, r;
+  if (!lane_position(i, per_tile, b, tok, r)) return;
+  const int64_t slice_stride = (int64_t)(N / 16) * per_tile;
+  f32x4_t d, u, unused;
+  slice_sum<kLinear>(down_partials, down_splits, slice_stride, i, 0, d, unused);
+  slice_sum<kLinear>(up_partials, up_splits, slice_stride, i, 0, u, unused);
+  const uint2 rs2 = pack4_pz(d[0], d[1], d[2], d[3]);
+  if (rs) *reinterpret_cast<uint2*>(rs + (int64_t)tok * N + r) = rs2;
+  float o[4] = {u[0], u[1], u[2], u[3]};
+  add_bf16x4(o, rs2);
+  *reinterpret_cast<uint2*>(out + (int64_t)tok * N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
 }
 
 int token_blocks(int b) {
@@ -434,6 +517,34 @@ hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   }
 }
 
+template <int NT, int W, int H>
+hipError_t group_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks, size_t lds,
+                        hipStream_t s) {
+  static bool attr_set = false;  // idempotent: every call sets the same maximum
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_group_kernel<NT, W, H>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((px_group_kernel<NT, W, H>), dim3(blocks), dim3(kWave * W), lds, s, a0, a1,
+                     blocks0);
+  return hipGetLastError();
+}
+
+template <int W, int H>
+hipError_t group_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
+                             size_t lds, hipStream_t s) {
+  switch (token_blocks(a0.b)) {
+    case 1: return group_launch<1, W, H>(a0, a1, blocks0, blocks, lds, s);
+    case 2: return group_launch<2, W, H>(a0, a1, blocks0, blocks, lds, s);
+    case 4: return group_launch<4, W, H>(a0, a1, blocks0, blocks, lds, s);
+    default:
+      if (H) return hipErrorInvalidValue;  // not planned (more than 4 token blocks)
+      return group_launch<8, W, 0>(a0, a1, blocks0, blocks, lds, s);
+  }
+}
+
 }  // namespace
 
 // CUs of the current device (256 on MI355X), read once.
@@ -457,6 +568,81 @@ ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const Pro
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
   const size_t tok = 16 * (size_t)token_blocks(b);  // padded tokens are stored too
   return (p.splits > 1 || always) ? sizeof(float) * (size_t)p.splits * tok * n_out : 0;
+}
+
+// The CUs split between the two projections (each keeping its K slices),
+// waves per block 7 or 8: the split that minimizes the longest wave stream
+// (units per wave times k steps per unit), then the fewest idle blocks.
+GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
+  const int cu = device_cu_count();
+  const int tok = 16 * token_blocks(b);
+  GroupPlan best{0, 0, 0, 0};
+  long long best_cost = -1;
+  int best_blocks = 0;
+  for (int w = 7; w <= 8; ++w) {
+    for (int bps0 = 1; bps0 * p0.splits < cu; ++bps0) {
+      const int bps1 = (cu - bps0 * p0.splits) / p1.splits;
+      if (bps1 < 1) break;
+      const long long pw0 = ((rows0 / 16) + (long long)bps0 * w - 1) / ((long long)bps0 * w);
+      const long long pw1 = ((rows1 / 16) + (long long)bps1 * w - 1) / ((long long)bps1 * w);
+      const long long c0 = pw0 * (p0.k_per_split / kKStep);
+      const long long c1 = pw1 * (p1.k_per_split / kKStep);
+      const long long cost = c0 > c1 ? c0 : c1;
+      const int blocks = bps0 * p0.splits + bps1 * p1.splits;
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && blocks > best_blocks)) {
+        best_cost = cost;
+        best_blocks = blocks;
+        best = GroupPlan{bps0, bps1, w, (tok <= 64 && pw0 <= 4 && pw1 <= 4) ? 4 : 0};
+      }
+    }
+  }
+  return best;  // waves == 0: the CUs cannot hold both grids
+}
+
+hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
+                       const ProjPlan& up, const GroupPlan& g, hipStream_t s) {
+  const int b = a.b;
+  const int ntb = token_blocks(b);
+  f32x4_t* part = reinterpret_cast<f32x4_t*>(a.partials);
+  f32x4_t* up_part = reinterpret_cast<f32x4_t*>(reinterpret_cast<char*>(a.partials) +
+                                                a.down_part_bytes);
+  // 1. gate/up partials
+  FxArgs gu{a.w_gate, a.w_upw, a.I, 2 * a.I, a.H, a.x, b, gate_up.k_per_split,
+            gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr};
+  hipError_t e = fx_dispatch(gu, gate_up, s);
+  if (e != hipSuccess) return e;
+  // 2. h from the gate/up partials, beside y from the latent partials
+  const int lat_waves = (a.L + kBlockCols - 1) / kBlockCols;
+  const int threads = kWave * lat_waves;
+  const int64_t red_items = (int64_t)(a.I / 16) * ntb * kWave;
+  const int red_blocks = (int)((red_items + threads - 1) / threads);
+  hipLaunchKernelGGL(tail_mid_kernel, dim3(red_blocks + b), dim3(threads), 0, s, part,
+                     gate_up.splits, b, ntb, a.I, a.h, red_blocks, a.lat, a.tp, a.L, a.gamma,
+                     a.eps, a.y);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // 3. down and up projections in one grid (the gate/up partials are consumed)
+  FxArgs dn{a.w_down, nullptr, a.H, a.H, a.I, a.h, b, down.k_per_split, g.bps0, down.pitch,
+            part, nullptr, nullptr};
+  FxArgs upa{a.w_up, nullptr, a.H, a.H, a.L, a.y, b, up.k_per_split, g.bps1, up.pitch, up_part,
+             nullptr, nullptr};
+  const int blocks0 = g.bps0 * down.splits;
+  const int blocks = blocks0 + g.bps1 * up.splits;
+  const size_t lds = down.lds > up.lds ? down.lds : up.lds;
+  if (g.waves == 7)
+    e = g.hold ? group_dispatch_nt<7, 4>(dn, upa, blocks0, blocks, lds, s)
+               : group_dispatch_nt<7, 0>(dn, upa, blocks0, blocks, lds, s);
+  else if (g.waves == 8)
+    e = g.hold ? group_dispatch_nt<8, 4>(dn, upa, blocks0, blocks, lds, s)
+               : group_dispatch_nt<8, 0>(dn, upa, blocks0, blocks, lds, s);
+  else
+    e = hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  // 4. rs, then out = up + rs
+  const int64_t out_items = (int64_t)(a.H / 16) * ntb * kWave;
+  hipLaunchKernelGGL(tail_out_kernel, dim3((unsigned)((out_items + 255) / 256)), dim3(256), 0, s,
+                     part, down.splits, up_part, up.splits, b, ntb, a.H, a.rs, a.out);
+  return hipGetLastError();
 }
 
 hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X, int b,

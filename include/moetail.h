@@ -9,8 +9,8 @@
  * Conventions for every entry point:
  *   - BF16 arrays are uint16_t bit patterns.  Every array pointer is a DEVICE
  *     pointer to dense row-major memory owned by the caller; the library
- *     keeps no pointer after the call returns and allocates nothing
- *     ([tail] BoundTail: "run is graph-capturable and allocates nothing").
+ *     keeps no pointer after the call returns and allocates nothing (as
+ *     the [tail] BoundTail run call is capturable and allocation-free).
  *     Scratch, where an entry point needs any, is the caller's workspace,
  *     sized by moetail_workspace_bytes.
  *   - BF16/FP32 array pointers must be 16-byte aligned (the kernels move
@@ -26,8 +26,8 @@
  *     captured into a HIP graph.  Results are deterministic: the same inputs
  *     give the same bits on every call.
  *   - Every BF16 word the library writes is rounded to nearest even from
- *     FP32, and a -0 result is written as +0 ([tail] _TpTailKernel: "-0.0 as
- *     +0.0"; [shared] SharedBase.push: "-0 made +0").
+ *     FP32, and a -0 result is written as +0 (the rule of the [tail]
+ *     _TpTailKernel epilogue and of the [shared] SharedBase.push stores).
  */
 #ifndef MOETAIL_H
 #define MOETAIL_H
@@ -57,6 +57,7 @@ extern "C" {
 #define MOETAIL_OP_TP_FINALIZE 1
 #define MOETAIL_OP_COMBINE_NORM_UPPROJ 2
 #define MOETAIL_OP_SHARED_EXPERT 3
+#define MOETAIL_OP_TAIL 4
 
 /* Limits.  P (and L) % 8 == 0 ([tail] 8-column fragments). */
 #define MOETAIL_MAX_WIDTH 8192  /* P, L: rows held in registers, 512 columns per wave */
@@ -67,7 +68,7 @@ extern "C" {
 #define MOETAIL_MAX_GEMM_K 32768    /* H and I of the shared expert */
 
 /*
- * EP finalize ([tail] module docstring, "With expert parallelism ..."):
+ * EP finalize ([tail] module docstring, the expert-parallel case):
  * for every simulated rank d and token t, over the routes k local to d in
  * ascending order, with x the route's row and w its weight,
  *     g       = fp32(gamma) + gain_center
@@ -103,7 +104,7 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank,
                      uint16_t* out, hipStream_t stream);
 
 /*
- * Expert-TP finalize ([tail] module docstring, "Under expert TP ...", and
+ * Expert-TP finalize ([tail] module docstring, the expert-TP case, and
  * _TpTailKernel): every rank holds a K-partial of every route row.
  *     x_r    = bf16(sum_{d=0}^{tp-1} fp32(kpartials[d][idx[t][k]]))  FP32 from +0.0
  *     out[t] = bf16(sum_k fp32(n(x_r) * w[t][k]))   routes in order, from +0.0
@@ -176,11 +177,42 @@ int moetail_shared_expert(const uint16_t* x, int b, int H,
                           hipStream_t stream);
 
 /*
+ * The decode tail after the finalize in one call ([tail_runtime] module
+ * docstring: the latent combine, RMSNorm and K-split up projection with the
+ * shared expert's reduce-scatter partial added; [shared] for that partial):
+ *     rs  = moetail_shared_expert(x)                       (as that call)
+ *     out = moetail_combine_norm_upproj(latent_partials, rs) (as that call)
+ * with the hidden width H as the up projection's output width N.  The
+ * results are the same bits as those two calls in that order; the work is
+ * five launches instead of eight: gate/up; {h, y}; {down, up} projections
+ * as one grid; {rs, out}.
+ *
+ *   latent_partials [tp][b][L], gamma [L], w_up [H][L]: as in
+ *                   moetail_combine_norm_upproj (N = H).
+ *   x [b][H], w_gate, w_upw [I][H], w_down [H][I]: as in
+ *                   moetail_shared_expert.
+ *   out             [b][H] BF16 written.
+ *   rs, normed, h   [b][H], [b][L], [b][I] BF16 written, or NULL (then kept
+ *                   in the workspace or not kept).
+ *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_TAIL, b, L,
+ *                   H, I) bytes, 256-byte aligned.
+ *   Limits: those of the two calls: b <= 128, 1 <= tp <= 32, L % 32 == 0,
+ *   L <= 8192, H % 64 == 0, I % 64 == 0, H, I <= MOETAIL_MAX_GEMM_K.
+ */
+int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
+                 float eps, const uint16_t* w_up, int L, const uint16_t* x,
+                 const uint16_t* w_gate, const uint16_t* w_upw,
+                 const uint16_t* w_down, int H, int I, int b, uint16_t* out,
+                 uint16_t* rs, uint16_t* normed, uint16_t* h, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Workspace bytes an operation needs (0 when none):
  *   MOETAIL_OP_FINALIZE:            0
  *   MOETAIL_OP_TP_FINALIZE:         dim0 = K, dim1 = P
  *   MOETAIL_OP_COMBINE_NORM_UPPROJ: dim0 = L, dim1 = N, dim2 = tp
  *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
+ *   MOETAIL_OP_TAIL:                dim0 = L, dim1 = H, dim2 = I
  * Returns 0 for an unknown op or out-of-range sizes.
  */
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);

@@ -11,8 +11,8 @@
  *     -ffp-contract=off: no fused multiply-add anywhere);
  *   * BF16 round-to-nearest-even exactly where the pages round;
  *   * a BF16 word that would be -0 is written as +0 where a result leaves
- *     a kernel ([tail] _TpTailKernel docstring: "-0.0 as +0.0"; [shared]
- *     SharedBase.push: "-0 made +0").
+ *     a kernel (the rule stated in the [tail] _TpTailKernel docstring and
+ *     at the [shared] SharedBase.push stores).
  *
  * Readings taken where the pages leave a step open are stated next to the
  * code that takes them.  Page keys ([tail], [tail_runtime], [shared]) are

@@ -27,10 +27,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(moetail_\w+)\s*\(", text)))
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-              "moetail_shared_expert", "moetail_workspace_bytes", "moetail_status_string"):
+              "moetail_shared_expert", "moetail_tail", "moetail_workspace_bytes",
+              "moetail_status_string"):
         assert n in names
     assert set(names) == set(mt.ENTRY_POINTS)
 
@@ -155,8 +156,40 @@ def test_shared_validation():
     assert _sh(ws=None, wsb=0) == mt.EWORKSPACE
 
 
+def _tail(ws=A, wsb=1 << 31, **kw):
+    a = dict(lat=A, tp=8, gamma=A, eps=1e-6, wup=A, L=3584, x=A, wg=A, wu=A, wd=A, H=7168,
+             I=6144, b=64, out=A, rs=None, normed=None, h=None)
+    a.update(kw)
+    return mt.lib().moetail_tail(a["lat"], a["tp"], a["gamma"], a["eps"], a["wup"], a["L"],
+                                 a["x"], a["wg"], a["wu"], a["wd"], a["H"], a["I"], a["b"],
+                                 a["out"], a["rs"], a["normed"], a["h"], ws, wsb, None)
+
+
+def test_tail_validation():
+    # every case is refused before anything launches (the pointers are fake)
+    assert _tail(b=0) == mt.OK
+    assert _tail(b=0, lat=None, x=None, ws=None, wsb=0) == mt.OK  # b == 0 before any check
+    assert _tail(out=None) == mt.EINVAL
+    assert _tail(x=None) == mt.EINVAL
+    assert _tail(wd=A + 2) == mt.EINVAL
+    assert _tail(rs=A + 8) == mt.EINVAL
+    assert _tail(eps=-1.0) == mt.EINVAL
+    assert _tail(tp=0) == mt.EINVAL
+    assert _tail(L=3600) == mt.EUNSUPPORTED
+    assert _tail(H=7200) == mt.EUNSUPPORTED
+    assert _tail(I=6100) == mt.EUNSUPPORTED
+    assert _tail(tp=33) == mt.EUNSUPPORTED
+    assert _tail(b=129) == mt.EUNSUPPORTED
+    assert _tail(ws=None, wsb=0) == mt.EWORKSPACE
+    assert _tail(wsb=16) == mt.EWORKSPACE
+    assert _tail(ws=A + 16) == mt.EWORKSPACE
+
+
 @pytest.mark.parametrize("b", [1, 8, 16, 32, 64, 128])
 def test_workspace_query(b):
+    tail = mt.workspace_bytes(mt.OP_TAIL, b, 3584, 7168, 6144)
+    assert tail >= b * (3584 + 6144) * 2 and tail % 256 == 0
+    assert mt.workspace_bytes(mt.OP_TAIL, b, 3600, 7168, 6144) == 0
     up = mt.workspace_bytes(mt.OP_COMBINE_NORM_UPPROJ, b, 3584, 7168, 8)
     assert up >= b * 3584 * 2 and up % 256 == 0
     sh = mt.workspace_bytes(mt.OP_SHARED_EXPERT, b, 7168, 6144)

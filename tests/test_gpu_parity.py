@@ -340,7 +340,7 @@ def run_shared(inp, with_h=True):
 
 
 def sample_tokens(b):
-    return sorted({0, 1, min(15, b - 1), min(16, b - 1), b // 2, b - 1})
+    return sorted(t for t in {0, 1, 15, 16, b // 2, b - 1} if t < b)
 
 
 @pytest.mark.parametrize("b", [16, 32, 64, 128])
@@ -519,3 +519,94 @@ def test_tail_step_two_stream_graph_matches_eager():
     _, want = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
                               nthreads=NT)
     assert np.array_equal(eager[0][0], want)
+
+
+# ------------------------------------------------------------- fused tail --
+
+def run_tail_and_calls(up, sh, with_opt=True):
+    """moetail_tail, and the two calls it stands for, on the same inputs."""
+    b, H, I, L, tp = sh["b"], sh["H"], sh["I"], up["L"], up["tp"]
+    lat, gamma, w_up = dev(up["lat"]), dev(up["gamma"]), dev(up["w_up"])
+    x, wg, wu, wd = dev(sh["x"]), dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"])
+    out = empty_bf16(b, H)
+    rs, normed, h = ((empty_bf16(b, H), empty_bf16(b, L), empty_bf16(b, I)) if with_opt
+                     else (None, None, None))
+    mt.moetail_tail(lat, gamma, up["eps"], w_up, x, wg, wu, wd, out, rs=rs, normed=normed, h=h,
+                    workspace=mt.new_workspace(mt.OP_TAIL, b, L, H, I))
+    rs2, h2, out2, normed2 = empty_bf16(b, H), empty_bf16(b, I), empty_bf16(b, H), empty_bf16(b, L)
+    mt.moetail_shared_expert(x, wg, wu, wd, rs2, h=h2,
+                             workspace=mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I))
+    mt.moetail_combine_norm_upproj(lat, gamma, up["eps"], w_up, out2, rs=rs2, normed=normed2,
+                                   workspace=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L, H,
+                                                              tp))
+    fused = dict(out=host(out), rs=host(rs) if rs is not None else None,
+                 normed=host(normed) if normed is not None else None,
+                 h=host(h) if h is not None else None)
+    calls = dict(out=host(out2), rs=host(rs2), normed=host(normed2), h=host(h2))
+    return fused, calls
+
+
+@pytest.mark.parametrize("b", [1, 32, 64, 128])
+def test_tail_equals_the_two_calls(b):
+    """b tokens of the decode tail: tp=8 latent partials [8, b, 3584], W_up
+    [7168, 3584], shared expert 7168 -> 6144 -> 7168."""
+    up = workloads.upproj(20 + b, b=b)
+    sh = workloads.shared(30 + b, b=b)
+    fused, calls = run_tail_and_calls(up, sh)
+    for k in ("out", "rs", "normed", "h"):
+        assert np.array_equal(fused[k], calls[k]), k
+    sel = sample_tokens(b)
+    want_h, want_rs = oracle.shared_expert(sh["x"][sel], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                           nthreads=NT)
+    gemm_bar(fused["rs"][sel], want_rs, f"tail rs b={b}")
+    gemm_bar(fused["h"][sel], want_h, f"tail h b={b}")
+    want_n, want_o = oracle.combine_norm_upproj(up["lat"][:, sel], up["gamma"], up["eps"],
+                                                up["w_up"], want_rs, nthreads=NT)
+    assert np.array_equal(fused["normed"][sel], want_n)
+    gemm_bar(fused["out"][sel], want_o, f"tail out b={b}")
+    fused2, _ = run_tail_and_calls(up, sh, with_opt=False)  # rs, y, h in the workspace
+    assert np.array_equal(fused2["out"], fused["out"])
+
+
+@pytest.mark.parametrize("b,tp,L,H,I", [(5, 3, 544, 256, 128), (17, 1, 32, 64, 64),
+                                        (40, 2, 1024, 512, 192), (3, 32, 8192, 128, 1024)])
+def test_tail_ragged(b, tp, L, H, I):
+    up = workloads.upproj(b + L, b=b, tp=tp, L=L, N=H)
+    sh = workloads.shared(b + H, b=b, H=H, I=I)
+    fused, calls = run_tail_and_calls(up, sh)
+    for k in ("out", "rs", "normed", "h"):
+        assert np.array_equal(fused[k], calls[k]), k
+    want_h, want_rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                           nthreads=NT)
+    gemm_bar(fused["rs"], want_rs, "tail rs")
+    want_n, want_o = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"],
+                                                want_rs, nthreads=NT)
+    assert np.array_equal(fused["normed"], want_n)
+    gemm_bar(fused["out"], want_o, "tail out")
+
+
+def test_tail_graph_replay():
+    up = workloads.upproj(5, b=64)
+    sh = workloads.shared(5, b=64)
+    lat, gamma, w_up = dev(up["lat"]), dev(up["gamma"]), dev(up["w_up"])
+    x, wg, wu, wd = dev(sh["x"]), dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"])
+    out, rs = empty_bf16(64, 7168), empty_bf16(64, 7168)
+    ws = mt.new_workspace(mt.OP_TAIL, 64, 3584, 7168, 6144)
+
+    def call():
+        mt.moetail_tail(lat, gamma, 1e-6, w_up, x, wg, wu, wd, out, rs=rs, workspace=ws)
+
+    call()
+    eager = (host(out), host(rs))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for _ in range(3):
+        out.fill_(SENTINEL)
+        rs.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), eager[0]) and np.array_equal(host(rs), eager[1])

@@ -40,14 +40,14 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
 
 
-# HBM bytes of one moetail_shared_expert call at b=64 (its four kernels), from
-# two rocprofv3 --pmc passes over `bench.py --steps 3 --warmup 1
-# --no-cpu-baseline --no-kernels --copy-calibration`: FETCH_SIZE and WRITE_SIZE
-# per dispatch, scaled by what each reads for the calibration kernel (256 MiB
-# in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the
-# kernel sources with this digest only.
-TRAFFIC = dict(source_digest="0b0997c8e4fe5b0b", fetch_bytes=310882 * 1024,
-               write_bytes=40576 * 1024)
+# HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
+# rocprofv3 --pmc passes over `bench.py --steps 3 --warmup 1 --no-cpu-baseline
+# --no-kernels --copy-calibration`: FETCH_SIZE and WRITE_SIZE per dispatch,
+# scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
+# out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
+# with this digest only.
+TRAFFIC = dict(source_digest="779ffd4e50d94a56", fetch_bytes=187892 * 2 * 1024,
+               write_bytes=49088 * 1024)
 
 
 def kernel_source_digest():
@@ -217,14 +217,14 @@ def main():
                      GBps=round(algo[n] / per_call[n] / 1e3, 1),
                      frac=round(algo[n] / per_call[n] / 1e3 / HBM_PEAK_GBPS, 4))
              for n in per_call}
-    dom = "shared_expert"
+    dom = "tail"
     traffic = traffic_bytes = None
     if kernel_source_digest() == TRAFFIC["source_digest"]:
         traffic_bytes = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
         traffic = round(traffic_bytes / per_call[dom] / 1e3, 1)
     roofline = dict(bound="hbm",
-                    kernel="moetail_shared_expert at b=64: gate/up and down projections with "
-                           "their split reductions (4 kernels, one call)",
+                    kernel="moetail_tail at b=64 (one call, four kernels: gate/up; h and y; "
+                           "down and up projections as one grid; rs and out)",
                     achieved=entry[dom]["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=entry[dom]["frac"], traffic=traffic, traffic_bytes=traffic_bytes,
                     algorithmic_bytes=algo[dom])

@@ -53,13 +53,16 @@ def lib():
         _lib.oracle_sum_of_squares.restype = F32
         _lib.oracle_finalize.argtypes = [P, I64, P, P, I32, P, F32, F32, I32,
                                          I32, I32, I32, I32, P, P, I32]
+        _lib.oracle_finalize_plain.argtypes = [P, I64, P, P, I32, I32, I32, I32, I32, P, P,
+                                               I32]
         _lib.oracle_rank_combine.argtypes = [P, I32, I32, I32, P]
         _lib.oracle_tp_finalize.argtypes = [P, I64, P, P, I32, P, F32, F32, I32,
                                             I32, I32, I32, I32, P, I32]
         _lib.oracle_combine_norm_upproj.argtypes = [P, I32, P, F32, P, I32, P,
                                                     I32, I32, P, P, I32]
         _lib.oracle_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, I32]
-        for f in ("oracle_bf16_round", "oracle_finalize", "oracle_rank_combine",
+        for f in ("oracle_bf16_round", "oracle_finalize", "oracle_finalize_plain",
+                  "oracle_rank_combine",
                   "oracle_tp_finalize", "oracle_combine_norm_upproj",
                   "oracle_shared_expert"):
             getattr(_lib, f).restype = None
@@ -120,6 +123,22 @@ def finalize(rows, idx, w, gamma, gain_center, eps, weight_before_norm,
     lib().oracle_finalize(_ptr(rows), R, _ptr(idx), _ptr(w), wdt, _ptr(gamma),
                           gain_center, eps, int(bool(weight_before_norm)),
                           b, K, P, tp, _ptr(partials), _ptr(out), nthreads)
+    return partials, out
+
+
+def finalize_plain(rows, idx, w, combine=True, nthreads=0):
+    """The finalize without a per-route norm ([tail_runtime] module docstring):
+    rows [tp,R,P] u16, idx [tp,b,K] i32, w [b,K] f32|u16.
+    Returns (partials [tp,b,P], out [b,P] or None)."""
+    rows = _u16(rows)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    w, wdt = _weights(w)
+    tp, R, P = rows.shape
+    _, b, K = idx.shape
+    partials = np.empty((tp, b, P), np.uint16)
+    out = np.empty((b, P), np.uint16) if combine else None
+    lib().oracle_finalize_plain(_ptr(rows), R, _ptr(idx), _ptr(w), wdt, b, K, P, tp,
+                                _ptr(partials), _ptr(out), nthreads)
     return partials, out
 
 

@@ -118,7 +118,7 @@ static float inv_rms(float ss, int P, float eps) {
  * weight_before_norm, then s_r * rsqrt(mean(s_r^2) + eps) times w_r;
  * without it the gain multiplies after the norm.  Order per element from
  * the helpers gains / normalized and the route weight multiplied last on
- * its own ("each product rounded alone"):
+ * its own (every product rounds separately):
  *   wbn:  v = x * g,  n = v * inv,           p = n * w
  *   else: v = x,      n = (x * inv) * g,     p = n * w
  * with g = fp32(gamma) + gain_center in FP32. */
@@ -196,6 +196,36 @@ void oracle_finalize(const uint16_t* rows, int64_t R, const int32_t* idx,
         free(acc);
     }
     free(gain);
+    if (out) oracle_rank_combine(partials, tp, b, P, out);
+}
+
+/* [tail_runtime] module docstring, the Kimi finalize: no per-route norm, the
+ * partial is the route-weighted sum of the token's local rows,
+ *   partial[d][t] = bf16(sum over local k, ascending, from +0.0, of
+ *                        fp32(x_k) * w_k)      (-0 written as +0)
+ * each product rounded on its own, then the same rank combine. */
+void oracle_finalize_plain(const uint16_t* rows, int64_t R, const int32_t* idx,
+                           const void* w, int w_dtype, int b, int K, int P, int tp,
+                           uint16_t* partials, uint16_t* out, int nthreads) {
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads())
+    for (int dt = 0; dt < tp * b; ++dt) {
+        int d = dt / b, t = dt % b;
+        float* acc = (float*)malloc(sizeof(float) * (size_t)P);
+        for (int c = 0; c < P; ++c) acc[c] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            int32_t r = idx[((int64_t)d * b + t) * K + k];
+            if (r < 0 || (int64_t)r >= R) continue;
+            const uint16_t* x = rows + ((int64_t)d * R + r) * P;
+            float wk = route_weight(w, w_dtype, (int64_t)t * K + k);
+            for (int c = 0; c < P; ++c) {
+                float prod = f32_of(x[c]) * wk;
+                acc[c] = acc[c] + prod;
+            }
+        }
+        uint16_t* dst = partials + ((int64_t)d * b + t) * P;
+        for (int c = 0; c < P; ++c) dst[c] = plus_zero(bf16_of(acc[c]));
+        free(acc);
+    }
     if (out) oracle_rank_combine(partials, tp, b, P, out);
 }
 

@@ -45,6 +45,11 @@ void oracle_finalize(const uint16_t* rows, int64_t R, const int32_t* idx,
                      int b, int K, int P, int tp,
                      uint16_t* partials, uint16_t* out, int nthreads);
 
+/* The finalize without a per-route norm (Kimi): route-weighted sum. */
+void oracle_finalize_plain(const uint16_t* rows, int64_t R, const int32_t* idx,
+                           const void* w, int w_dtype, int b, int K, int P, int tp,
+                           uint16_t* partials, uint16_t* out, int nthreads);
+
 /* Rank-order combine: out[b][P] = bf16(sum over d of partials[d][b][P]). */
 void oracle_rank_combine(const uint16_t* partials, int tp, int b, int P,
                          uint16_t* out);

@@ -480,3 +480,81 @@ def test_route_order_golden():
         out = oracle.tp_finalize(ones[None], np.arange(K, dtype=np.int32).reshape(1, K),
                                  w, gamma, case["gain_center"], case["eps"], wbn)
         assert hexes(out) == [case["expected_out_hex"]] * P
+
+
+# ------------------------------- finalize without a per-route norm (Kimi) --
+
+def test_plain_single_route_is_the_row():
+    # one route, w = 1, tp = 1: every product is exact, the sum is the row
+    rng = np.random.default_rng(21)
+    x = bits(rng.standard_normal((1, 1, 3584)) * 5)
+    x[0, 0, :3] = [0x8000, 0x0001, 0x8001]  # -0, the smallest denormals
+    p, out = oracle.finalize_plain(x, np.zeros((1, 1, 1), np.int32), np.ones((1, 1), np.float32))
+    want = x[0].copy()
+    want[want == 0x8000] = 0
+    assert np.array_equal(out, want) and np.array_equal(p[0], want)
+
+
+def test_plain_power_of_two_weights_exact():
+    # weights 1/2, 1/4, 1/8: products exact; with rows of BF16 values within a
+    # few binades the FP32 sum is exact too, so out = bf16 of the FP64 sum
+    rng = np.random.default_rng(22)
+    K, P = 3, 512
+    rows = bits(rng.uniform(1.0, 2.0, (1, K, P)))
+    w = np.array([[0.5, 0.25, 0.125]], np.float32)
+    _, out = oracle.finalize_plain(rows, np.arange(K, dtype=np.int32).reshape(1, 1, K), w)
+    exact = (ref.f64(rows[0]) * w[0][:, None].astype(np.float64)).sum(axis=0)
+    assert np.array_equal(out[0], oracle.bf16_round(ref.round_bf16(exact).astype(np.float32)))
+
+
+def test_plain_route_order_and_rank_order():
+    # routes (2^25, -2^25, 1) in order sum to 1.0; a rank per route: the same
+    P = 8
+    rows = bits(np.ones((1, 3, P)))
+    w = np.array([[2.0 ** 25, -2.0 ** 25, 1.0]], np.float32)
+    _, out = oracle.finalize_plain(rows, np.arange(3, dtype=np.int32).reshape(1, 1, 3), w)
+    assert hexes(out) == ["3f80"] * P
+    rows3 = np.repeat(bits(np.ones((1, 1, P))), 3, axis=0)
+    idx = np.full((3, 1, 3), -1, np.int32)
+    for d in range(3):
+        idx[d, 0, d] = 0
+    partials, out = oracle.finalize_plain(rows3, idx, w)
+    assert [hexes(partials[d])[0] for d in range(3)] == ["4c00", "cc00", "3f80"]
+    assert hexes(out) == ["3f80"] * P
+
+
+def test_plain_zero_weights_and_absent_routes():
+    rng = np.random.default_rng(23)
+    rows, idx, w, _ = _random_ep(rng, 3, 4, 64, 2)
+    p, out = oracle.finalize_plain(rows, idx, np.zeros_like(w))
+    assert not p.any() and not out.any()  # +0 everywhere, never 0x8000
+    R = rows.shape[1]
+    big = np.where(idx < 0, R + 5, idx).astype(np.int32)
+    a = oracle.finalize_plain(rows, idx, w)
+    c = oracle.finalize_plain(rows, big, w)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+@pytest.mark.parametrize("P,K,tp", [(8, 1, 1), (64, 3, 3), (520, 4, 2), (3584, 16, 8)])
+def test_plain_brute_force_fp64(P, K, tp):
+    """FP64 straight-line sum of w_k x_k per rank: the FP32 result lies within
+    the FP32 summation bound, and out within the combine's bound."""
+    rng = np.random.default_rng(P + K + tp)
+    rows, idx, w, _ = _random_ep(rng, 3, K, P, tp)
+    partials, out = oracle.finalize_plain(rows, idx, w)
+    b = idx.shape[1]
+    R = rows.shape[1]
+    acc = np.zeros((tp, b, P))
+    mag = np.zeros((tp, b, P))
+    for d in range(tp):
+        for t in range(b):
+            for k in range(K):
+                r = idx[d, t, k]
+                if 0 <= r < R:
+                    term = ref.f64(rows[d, r]) * float(w[t, k])
+                    acc[d, t] += term
+                    mag[d, t] += np.abs(term)
+    E = (K + 1) * U24 * mag
+    assert ref.within(partials, acc, E).all()
+    E_out = (E + ref.ulp_bf16(np.abs(acc) + E)).sum(axis=0) + 2 * tp * U24 * np.abs(acc).sum(axis=0)
+    assert ref.within(out, acc.sum(axis=0), E_out).all()

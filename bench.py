@@ -54,7 +54,8 @@ def kernel_source_digest():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "expert_finalize_rmsnorm_amd", "csrc")
-    for name in ("common.h", "kernels.h", "project.hip", "api.hip", "finalize.hip"):
+    # the sources of the fused tail's kernels and of its launch plans
+    for name in ("common.h", "kernels.h", "norm_device.h", "project.hip", "api.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -344,6 +345,15 @@ def config_kernels(base, log):
     us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], base["gamma"],
                                              1.0, 1e-6, True, partials=part), 48)
     add("finalize b=64, partials only", us, fin_in + TP * B * P * 2,
+        tokens_per_s=round(B / (us * 1e-6), 1))
+    # without a per-route norm (the Kimi finalize): partials, and out only
+    us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], None, 0.0, 1e-6,
+                                             mt.NO_NORM, partials=part), 48)
+    add("finalize, no norm (Kimi) b=64, partials only", us, fin_in - P * 2 + TP * B * P * 2,
+        tokens_per_s=round(B / (us * 1e-6), 1))
+    us = timed(lambda i: mt.moetail_finalize(rows[i], base["idx"], base["w"], None, 0.0, 1e-6,
+                                             mt.NO_NORM, out=out), 48)
+    add("finalize+combine, no norm (Kimi) b=64, out only", us, fin_in - P * 2 + B * P * 2,
         tokens_per_s=round(B / (us * 1e-6), 1))
     del rows
 

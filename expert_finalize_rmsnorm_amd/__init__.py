@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libmoetail.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
+NORM_GAIN_AFTER, NORM_GAIN_FIRST, NO_NORM = 0, 1, 2  # moetail_finalize norm modes
 OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL = 0, 1, 2, 3, 4
 
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
@@ -114,8 +115,10 @@ def workspace_bytes(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0) ->
 
 def moetail_finalize(rows, permuted_idx, route_w, gamma, gain_center, eps, weight_before_norm,
                      partials=None, out=None, stream=None):
-    """rows [tp, R, P], permuted_idx [tp, b, K], route_w [b, K], gamma [P];
-    writes partials [tp, b, P] and/or out [b, P]."""
+    """rows [tp, R, P], permuted_idx [tp, b, K], route_w [b, K], gamma [P]
+    (or None with NO_NORM); writes partials [tp, b, P] and/or out [b, P].
+    weight_before_norm: a bool, or a norm mode (NORM_GAIN_AFTER,
+    NORM_GAIN_FIRST, NO_NORM)."""
     _bf16(rows, "rows"), _bf16(gamma, "gamma"), _bf16(partials, "partials"), _bf16(out, "out")
     tp, R, P = rows.shape
     _, b, K = permuted_idx.shape
@@ -123,7 +126,7 @@ def moetail_finalize(rows, permuted_idx, route_w, gamma, gain_center, eps, weigh
         raise TypeError("permuted_idx must be int32")
     st = lib().moetail_finalize(_ptr(rows), R, _ptr(permuted_idx), _ptr(route_w),
                                 _weights(route_w), _ptr(gamma), float(gain_center), float(eps),
-                                int(bool(weight_before_norm)), b, K, P, tp, _ptr(partials),
+                                int(weight_before_norm), b, K, P, tp, _ptr(partials),
                                 _ptr(out), _stream(stream))
     _check(st, "moetail_finalize")
 

@@ -22,12 +22,12 @@ bool a16(const void* p) { return p != nullptr && aligned(p, 16); }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int check_norm_args(const void* w, int w_dtype, const uint16_t* gamma, float eps, int K, int P,
-                    int tp, int b) {
+                    int tp, int b, bool uses_gamma = true) {
   if (b < 0 || K <= 0 || P <= 0 || tp <= 0) return MOETAIL_EINVAL;
   if (w_dtype != MOETAIL_F32 && w_dtype != MOETAIL_BF16) return MOETAIL_EINVAL;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;  // rejects NaN too
   if (w == nullptr || !aligned(w, w_dtype == MOETAIL_F32 ? 4 : 2)) return MOETAIL_EINVAL;
-  if (!a16(gamma)) return MOETAIL_EINVAL;
+  if (uses_gamma ? !a16(gamma) : (gamma && !aligned(gamma, 16))) return MOETAIL_EINVAL;
   if (P % 8 || P > MOETAIL_MAX_WIDTH || K > MOETAIL_MAX_ROUTES || tp > MOETAIL_MAX_TP ||
       b > MOETAIL_MAX_TOKENS)
     return MOETAIL_EUNSUPPORTED;
@@ -118,7 +118,10 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
                      float gain_center, float eps, int weight_before_norm, int b, int K, int P,
                      int tp, uint16_t* partials, uint16_t* out, hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
-  int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b);
+  if (weight_before_norm < MOETAIL_NORM_GAIN_AFTER || weight_before_norm > MOETAIL_NO_NORM)
+    return MOETAIL_EINVAL;
+  int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b,
+                           weight_before_norm != MOETAIL_NO_NORM);
   if (st) return st;
   if (!a16(rows) || rows_per_rank <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4))
     return MOETAIL_EINVAL;
@@ -126,7 +129,7 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
   if ((partials && !a16(partials)) || (out && !a16(out))) return MOETAIL_EINVAL;
   if (!__builtin_isfinite(gain_center)) return MOETAIL_EINVAL;
   EpArgs a{rows, rows_per_rank, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
-           gain_center, eps, weight_before_norm != 0, b, K, P, tp, partials, out};
+           gain_center, eps, weight_before_norm, b, K, P, tp, partials, out};
   return hip_status(launch_ep_finalize(a, stream));
 }
 
@@ -136,6 +139,7 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32
                         int tp, uint16_t* out, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
+  if (weight_before_norm != 0 && weight_before_norm != 1) return MOETAIL_EINVAL;
   int st = check_norm_args(route_w, route_w_dtype, gamma, eps, K, P, tp, b);
   if (st) return st;
   if (!a16(kpartials) || num_rows <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4) ||

@@ -35,8 +35,15 @@ __device__ __forceinline__ float load_weight(const void* w, int64_t i) {
   return reinterpret_cast<const float*>(w)[i];
 }
 
-// Normalized, route-weighted products of one chunk, added into acc.
-template <bool WBN>
+// Norm modes: kGainAfter (the gain multiplies the normalized row), kGainFirst
+// (weight_before_norm: the gain multiplies before the statistic) and kNoNorm
+// ([tail_runtime] module docstring, the Kimi finalize: the route-weighted
+// row itself, no statistic).
+enum { kGainAfter = 0, kGainFirst = 1, kNoNorm = 2 };
+
+// Route-weighted products of one chunk (normalized unless kNoNorm), added
+// into acc.
+template <int MODE>
 __device__ __forceinline__ void add_products(const uint4& xq, const float (&g)[8], float inv,
                                              float w, float (&acc)[8]) {
   float x[8];
@@ -44,24 +51,26 @@ __device__ __forceinline__ void add_products(const uint4& xq, const float (&g)[8
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     float n;
-    if (WBN) {
+    if (MODE == kGainFirst) {
       float s = x[c] * g[c];
       n = s * inv;
-    } else {
+    } else if (MODE == kGainAfter) {
       float u = x[c] * inv;
       n = u * g[c];
+    } else {
+      n = x[c];
     }
     float p = n * w;
     acc[c] = acc[c] + p;
   }
 }
 
-// Lane's share of a chunk's sum of squares (the gains first with WBN).
-template <bool WBN>
+// Lane's share of a chunk's sum of squares (the gains first with kGainFirst).
+template <int MODE>
 __device__ __forceinline__ float chunk_ss(const uint4& xq, const float (&g)[8]) {
   float v[8];
   unpack8(xq, v);
-  if (WBN) {
+  if (MODE == kGainFirst) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) v[c] = v[c] * g[c];
   }
@@ -117,7 +126,7 @@ struct Pair {
 
 // kSlots rows in flight per lane: 16 when the block has at most 8 waves
 // (256 VGPRs per lane), 8 for wider rows (up to 16 waves, 128 VGPRs).
-template <bool WBN, bool WBF16, int kSlots, int kMaxThreads>
+template <int MODE, bool WBF16, int kSlots, int kMaxThreads>
 __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
   __shared__ Pair pairs[kMaxPairs];
   __shared__ float block_ss[kSlots][16];
@@ -138,7 +147,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
   const int col = (wave * kWave + lane) * kChunk;
   const bool has = col < P;
   const int colc = has ? col : P - kChunk;  // lanes past the row read a valid chunk
-  const uint4 gq = load16(a.gamma + colc);
+  const uint4 gq = MODE != kNoNorm ? load16(a.gamma + colc) : make_uint4(0, 0, 0, 0);
   if (wave == 0) {
     const int nent = a.dense ? a.K : a.tp * a.K;
     const int ngroups = (nent + kWave - 1) / kWave;
@@ -215,23 +224,25 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
     }
     // All slots reduce without branches (slots past nb repeat the last
     // pair and are never used), so the slots' butterflies interleave.
-    float ss[kSlots];
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      ss[s] = has ? chunk_ss<WBN>(xq[s], g) : 0.0f;
-      ss[s] = wave_butterfly_sum(ss[s]);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int s = 0; s < kSlots; ++s)
-        if (s < nb) block_ss[s][wave] = ss[s];
-    }
-    __syncthreads();
     float my_inv = 0.0f;
-    if (lane < nb) {
-      float total = 0.0f;
-      for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
-      my_inv = inv_rms(total, inv_width, a.eps);
+    if (MODE != kNoNorm) {
+      float ss[kSlots];
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        ss[s] = has ? chunk_ss<MODE>(xq[s], g) : 0.0f;
+        ss[s] = wave_butterfly_sum(ss[s]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s)
+          if (s < nb) block_ss[s][wave] = ss[s];
+      }
+      __syncthreads();
+      if (lane < nb) {
+        float total = 0.0f;
+        for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
+        my_inv = inv_rms(total, inv_width, a.eps);
+      }
     }
     if (prod) {
 #pragma unroll
@@ -239,11 +250,11 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
         if (s < nb) {
           emit_through(readlane_i(mine.rank, s));
           const float inv = readlane_f(my_inv, s);
-          add_products<WBN>(xq[s], g, inv, readlane_f(mine.w, s), acc);
+          add_products<MODE>(xq[s], g, inv, readlane_f(mine.w, s), acc);
         }
       }
     }
-    __syncthreads();  // block_ss is refilled by the next batch
+    if (MODE != kNoNorm) __syncthreads();  // block_ss is refilled by the next batch
   }
   if (!prod) return;
   emit_through(a.tp);
@@ -252,7 +263,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
 
 // Column groups per token: enough blocks for one per CU (a block holds
 // a CU: up to 16 waves of up to 209 VGPRs), at most one group per wave.
-template <bool WBN, bool WBF16>
+template <int MODE, bool WBF16>
 hipError_t finalize_launch(FinArgs a, hipStream_t s) {
   const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;
   const int want = (device_cu_count() + a.b - 1) / a.b;
@@ -260,21 +271,23 @@ hipError_t finalize_launch(FinArgs a, hipStream_t s) {
   a.wpq = (nwaves + groups - 1) / groups;
   const dim3 grid(a.b, (nwaves + a.wpq - 1) / a.wpq);
   if (nwaves <= 8)
-    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 16, 512>), grid, dim3(kWave * nwaves), 0, s,
+    hipLaunchKernelGGL((finalize_kernel<MODE, WBF16, 16, 512>), grid, dim3(kWave * nwaves), 0, s,
                        a);
   else
-    hipLaunchKernelGGL((finalize_kernel<WBN, WBF16, 8, 1024>), grid, dim3(kWave * nwaves), 0, s,
+    hipLaunchKernelGGL((finalize_kernel<MODE, WBF16, 8, 1024>), grid, dim3(kWave * nwaves), 0, s,
                        a);
   return hipGetLastError();
 }
 
-hipError_t finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_t s) {
-  const int key = (wbn ? 2 : 0) | (w_bf16 ? 1 : 0);
-  switch (key) {
-    case 0: return finalize_launch<false, false>(a, s);
-    case 1: return finalize_launch<false, true>(a, s);
-    case 2: return finalize_launch<true, false>(a, s);
-    default: return finalize_launch<true, true>(a, s);
+hipError_t finalize_dispatch(const FinArgs& a, int mode, bool w_bf16, hipStream_t s) {
+  switch (mode * 2 + (w_bf16 ? 1 : 0)) {
+    case 0: return finalize_launch<kGainAfter, false>(a, s);
+    case 1: return finalize_launch<kGainAfter, true>(a, s);
+    case 2: return finalize_launch<kGainFirst, false>(a, s);
+    case 3: return finalize_launch<kGainFirst, true>(a, s);
+    case 4: return finalize_launch<kNoNorm, false>(a, s);
+    case 5: return finalize_launch<kNoNorm, true>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -287,7 +300,7 @@ hipError_t finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_
 // so no LDS pass or barrier precedes the row loads.  A block reads only its
 // rank's rows, so a token's rows spread over tp blocks.  The partial is the
 // fused kernel's bit for bit: the same chunks, tree, inverse and route order.
-template <bool WBN, bool WBF16, int kSlots, int kMaxThreads>
+template <int MODE, bool WBF16, int kSlots, int kMaxThreads>
 __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
   __shared__ float block_ss[kSlots][16];
   const int lane = threadIdx.x & (kWave - 1);
@@ -299,7 +312,7 @@ __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
   const int col = (wave * kWave + lane) * kChunk;
   const bool has = col < P;
   const int colc = has ? col : P - kChunk;
-  const uint4 gq = load16(a.gamma + colc);
+  const uint4 gq = MODE != kNoNorm ? load16(a.gamma + colc) : make_uint4(0, 0, 0, 0);
   int e = -1;
   float wk = 0.0f;
   if (lane < a.K) {
@@ -333,30 +346,32 @@ __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
       xq[s] = load16(rank_rows + (int64_t)row * P + colc);
     }
     mask = m;
-    float ss[kSlots];
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      ss[s] = has ? chunk_ss<WBN>(xq[s], g) : 0.0f;
-      ss[s] = wave_butterfly_sum(ss[s]);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int s = 0; s < kSlots; ++s)
-        if (s < nb) block_ss[s][wave] = ss[s];
-    }
-    __syncthreads();
     float my_inv = 0.0f;
-    if (lane < nb) {
-      float total = 0.0f;
-      for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
-      my_inv = inv_rms(total, inv_width, a.eps);
+    if (MODE != kNoNorm) {
+      float ss[kSlots];
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        ss[s] = has ? chunk_ss<MODE>(xq[s], g) : 0.0f;
+        ss[s] = wave_butterfly_sum(ss[s]);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s)
+          if (s < nb) block_ss[s][wave] = ss[s];
+      }
+      __syncthreads();
+      if (lane < nb) {
+        float total = 0.0f;
+        for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
+        my_inv = inv_rms(total, inv_width, a.eps);
+      }
     }
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
       if (s < nb)
-        add_products<WBN>(xq[s], g, readlane_f(my_inv, s), readlane_f(wk, ks[s]), acc);
+        add_products<MODE>(xq[s], g, readlane_f(my_inv, s), readlane_f(wk, ks[s]), acc);
     }
-    __syncthreads();  // block_ss is refilled by the next batch
+    if (MODE != kNoNorm) __syncthreads();  // block_ss is refilled by the next batch
   }
   if (has) store16(a.partials + ((int64_t)d * a.b + t) * P + col, pack8_pz(acc));
 }
@@ -395,34 +410,36 @@ __global__ void __launch_bounds__(256) rank_combine_kernel(const uint16_t* parti
 // as 4, 8 or 16 slots (8 at most for rows wider than 4096 columns, whose
 // 16-wave blocks leave 128 VGPRs a lane); a rank holding more takes more
 // batches.
-template <bool WBN, bool WBF16>
+template <int MODE, bool WBF16>
 hipError_t rank_finalize_launch(const FinArgs& a, hipStream_t s) {
   const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;
   const int expect = (a.K + a.tp - 1) / a.tp;
   const dim3 grid(a.b, a.tp), block(kWave * nwaves);
   if (nwaves <= 8) {
     if (expect <= 4)
-      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 4, 512>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rank_finalize_kernel<MODE, WBF16, 4, 512>), grid, block, 0, s, a);
     else if (expect <= 8)
-      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 8, 512>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rank_finalize_kernel<MODE, WBF16, 8, 512>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 16, 512>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rank_finalize_kernel<MODE, WBF16, 16, 512>), grid, block, 0, s, a);
   } else {
     if (expect <= 4)
-      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 4, 1024>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rank_finalize_kernel<MODE, WBF16, 4, 1024>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((rank_finalize_kernel<WBN, WBF16, 8, 1024>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((rank_finalize_kernel<MODE, WBF16, 8, 1024>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
-hipError_t rank_finalize_dispatch(const FinArgs& a, bool wbn, bool w_bf16, hipStream_t s) {
-  const int key = (wbn ? 2 : 0) | (w_bf16 ? 1 : 0);
-  switch (key) {
-    case 0: return rank_finalize_launch<false, false>(a, s);
-    case 1: return rank_finalize_launch<false, true>(a, s);
-    case 2: return rank_finalize_launch<true, false>(a, s);
-    default: return rank_finalize_launch<true, true>(a, s);
+hipError_t rank_finalize_dispatch(const FinArgs& a, int mode, bool w_bf16, hipStream_t s) {
+  switch (mode * 2 + (w_bf16 ? 1 : 0)) {
+    case 0: return rank_finalize_launch<kGainAfter, false>(a, s);
+    case 1: return rank_finalize_launch<kGainAfter, true>(a, s);
+    case 2: return rank_finalize_launch<kGainFirst, false>(a, s);
+    case 3: return rank_finalize_launch<kGainFirst, true>(a, s);
+    case 4: return rank_finalize_launch<kNoNorm, false>(a, s);
+    case 5: return rank_finalize_launch<kNoNorm, true>(a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -487,8 +504,8 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
 hipError_t launch_ep_finalize(const EpArgs& a, hipStream_t s) {
   FinArgs f{a.rows, a.R, a.idx, a.R, 0, a.w, a.gamma, a.gain_center, a.eps,
             a.b, a.K, a.P, a.tp, a.partials, a.out, 1};
-  if (!a.partials) return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
-  hipError_t e = rank_finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
+  if (!a.partials) return finalize_dispatch(f, a.wbn, a.w_bf16 != 0, s);
+  hipError_t e = rank_finalize_dispatch(f, a.wbn, a.w_bf16 != 0, s);
   if (e != hipSuccess || !a.out) return e;
   const int64_t threads = (int64_t)a.b * (a.P / kChunk);
   hipLaunchKernelGGL(rank_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
@@ -506,7 +523,7 @@ hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   FinArgs f{a.xr, 0, a.idx, a.num_rows, 1, a.w, a.gamma, a.gain_center, a.eps,
             a.b, a.K, a.P, 1, nullptr, a.out, 1};
-  return finalize_dispatch(f, a.wbn != 0, a.w_bf16 != 0, s);
+  return finalize_dispatch(f, a.wbn != 0 ? kGainFirst : kGainAfter, a.w_bf16 != 0, s);
 }
 
 hipError_t launch_latent_norm(const uint16_t* lat, int tp, int b, int L, const uint16_t* gamma,

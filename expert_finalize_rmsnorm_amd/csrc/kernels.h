@@ -21,7 +21,7 @@ struct EpArgs {
   int w_bf16;
   const uint16_t* gamma;  // [P]
   float gain_center, eps;
-  int wbn;
+  int wbn;  // norm mode: 0 gain after the norm, 1 gain first, 2 no norm
   int b, K, P, tp;
   uint16_t* partials;     // [tp][b][P] or null
   uint16_t* out;          // [b][P] or null

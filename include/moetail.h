@@ -52,6 +52,11 @@ extern "C" {
 #define MOETAIL_F32 0
 #define MOETAIL_BF16 1
 
+/* Norm modes of moetail_finalize (its weight_before_norm argument). */
+#define MOETAIL_NORM_GAIN_AFTER 0 /* n = (x * inv) * g */
+#define MOETAIL_NORM_GAIN_FIRST 1 /* weight_before_norm: s = x * g, n = s * inv */
+#define MOETAIL_NO_NORM 2         /* [tail_runtime] Kimi finalize: n = x */
+
 /* Operation ids for moetail_workspace_bytes. */
 #define MOETAIL_OP_FINALIZE 0
 #define MOETAIL_OP_TP_FINALIZE 1
@@ -78,13 +83,19 @@ extern "C" {
  *     partial = bf16(sum_k n * w)              FP32 from +0.0
  * and, when `out` is given, the rank combine ([tail] _TailReduceKernel)
  *     out[t]  = bf16(sum_{d=0}^{tp-1} fp32(partial[d][t]))   FP32 from +0.0.
+ * weight_before_norm is the norm mode: MOETAIL_NORM_GAIN_AFTER (0, false),
+ * MOETAIL_NORM_GAIN_FIRST (1, true), or MOETAIL_NO_NORM (2: the finalize of
+ * the [tail_runtime] module docstring, with no per-route norm,
+ *     partial = bf16(sum_k fp32(x) * w)        FP32 from +0.0,
+ * where gamma, gain_center and eps are not used and gamma may be NULL).
  *
  *   rows          [tp][rows_per_rank][P] BF16: rank d's GEMM2 output rows.
  *   permuted_idx  [tp][b][K] int32: row of route k of token t in rank d's
  *                 rows; a value outside [0, rows_per_rank) means the route
  *                 is not local to rank d (it contributes nothing there).
  *   route_w       [b][K] FP32 or BF16 (route_w_dtype): full top-K weights.
- *   gamma         [P] BF16 norm weight (ones when the norm has none).
+ *   gamma         [P] BF16 norm weight (ones when the norm has none); NULL
+ *                 allowed with MOETAIL_NO_NORM.
  *   partials      [tp][b][P] BF16 written (the resident rank-partial
  *                 buffer), or NULL when only `out` is wanted.
  *   out           [b][P] BF16 written, or NULL for partials only.

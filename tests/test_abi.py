@@ -165,6 +165,19 @@ def _tail(ws=A, wsb=1 << 31, **kw):
                                  a["out"], a["rs"], a["normed"], a["h"], ws, wsb, None)
 
 
+def test_finalize_norm_mode_validation():
+    lib = mt.lib()
+    for mode in (-1, 3):
+        assert lib.moetail_finalize(A, 8, A, A, mt.F32, A, 1.0, 1e-6, mode, 4, 16, 3584, 8, A, A,
+                                    None) == mt.EINVAL
+    # the expert-TP finalize takes the two normalizing modes only
+    assert lib.moetail_tp_finalize(A, 64, A, A, mt.F32, A, 1.0, 1e-6, mt.NO_NORM, 4, 16, 3584, 8,
+                                   A, A, 1 << 30, None) == mt.EINVAL
+    # gamma may be NULL only without a norm (checked before anything launches)
+    assert lib.moetail_finalize(A, 8, A, A, mt.F32, None, 1.0, 1e-6, mt.NORM_GAIN_FIRST, 4, 16,
+                                3584, 8, A, A, None) == mt.EINVAL
+
+
 def test_tail_validation():
     # every case is refused before anything launches (the pointers are fake)
     assert _tail(b=0) == mt.OK

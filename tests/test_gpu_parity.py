@@ -610,3 +610,79 @@ def test_tail_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(out), eager[0]) and np.array_equal(host(rs), eager[1])
+
+
+# ------------------------------- finalize without a per-route norm (Kimi) --
+
+def run_plain(inp, wkey="w32", mode="both", gamma=True):
+    tp, b, P = inp["tp"], inp["b"], inp["P"]
+    partials = empty_bf16(tp, b, P) if mode in ("both", "partials") else None
+    out = empty_bf16(b, P) if mode in ("both", "out") else None
+    mt.moetail_finalize(dev(inp["rows"]), dev(inp["idx"]), dev(inp[wkey]),
+                        dev(inp["gamma"]) if gamma else None, 0.0, 1e-6, mt.NO_NORM,
+                        partials=partials, out=out)
+    return (host(partials) if partials is not None else None,
+            host(out) if out is not None else None)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("wkey", ["w32", "w16"])
+def test_plain_decode_scale(seed, wkey):
+    """b=64, top-16 over tp=8 ranks, P=3584: the route-weighted sum, all modes."""
+    inp = workloads.ep_finalize(seed)
+    want_p, want_o = oracle.finalize_plain(inp["rows"], inp["idx"], inp[wkey], nthreads=NT)
+    got_p, got_o = run_plain(inp, wkey)
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+    _, only_o = run_plain(inp, wkey, "out", gamma=False)
+    only_p, _ = run_plain(inp, wkey, "partials", gamma=False)
+    assert np.array_equal(only_o, want_o) and np.array_equal(only_p, want_p)
+
+
+def test_plain_expanded_rows():
+    """The Kimi layout: one rank, expanded rows [b*K, P] with row t*K + k."""
+    b, K, P = 64, 16, 3584
+    rng = np.random.default_rng(31)
+    rows = bits(rng.standard_normal((1, b * K, P)) * 2)
+    idx = np.arange(b * K, dtype=np.int32).reshape(1, b, K)
+    g0 = torch.Generator("cpu").manual_seed(31)
+    w32, w16 = workloads.route_weights(g0, b, K)
+    inp = dict(rows=rows, idx=idx, w32=w32, w16=w16, gamma=np.zeros(P, np.uint16), tp=1, b=b,
+               P=P)
+    for wkey in ("w32", "w16"):
+        want_p, want_o = oracle.finalize_plain(rows, idx, inp[wkey], nthreads=NT)
+        for mode in ("out", "partials"):
+            got_p, got_o = run_plain(inp, wkey, mode, gamma=False)
+            if got_o is not None:
+                assert np.array_equal(got_o, want_o)
+            if got_p is not None:
+                assert np.array_equal(got_p, want_p)
+
+
+@pytest.mark.parametrize("b,K,P,tp", [(5, 3, 520, 3), (3, 7, 8, 1), (2, 32, 8192, 4),
+                                      (17, 8, 7168, 8), (3, 32, 64, 32)])
+def test_plain_ragged(b, K, P, tp):
+    if K % tp == 0:
+        inp = workloads.ep_finalize(b * 5 + K, b=b, K=K, P=P, tp=tp, outlier_frac=0.05)
+    else:
+        inp = workloads.ep_finalize(b, b=b, K=K, P=P, tp=1, outlier_frac=0.0)
+        rows1 = inp["rows"][0]
+        idx = np.full((tp, b, K), -1, np.int32)
+        for k in range(K):
+            idx[k % tp, :, k] = inp["idx"][0, :, k]
+        inp.update(rows=np.ascontiguousarray(np.broadcast_to(rows1, (tp,) + rows1.shape)),
+                   idx=idx, tp=tp)
+    want_p, want_o = oracle.finalize_plain(inp["rows"], inp["idx"], inp["w32"], nthreads=NT)
+    got_p, got_o = run_plain(inp)
+    assert np.array_equal(got_p, want_p) and np.array_equal(got_o, want_o)
+    _, only_o = run_plain(inp, mode="out")
+    assert np.array_equal(only_o, want_o)
+
+
+def test_plain_route_order():
+    P = 8
+    inp = dict(rows=bits(np.ones((1, 3, P))), idx=np.arange(3, dtype=np.int32).reshape(1, 1, 3),
+               w32=np.array([[2.0 ** 25, -2.0 ** 25, 1.0]], np.float32),
+               gamma=np.zeros(P, np.uint16), tp=1, b=1, P=P)
+    for mode in ("out", "both"):
+        _, got_o = run_plain(inp, mode=mode, gamma=False)
+        assert [f"{int(v):04x}" for v in got_o.ravel()] == ["3f80"] * P

@@ -46,7 +46,7 @@ METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
 # scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
 # out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
 # with this digest only.
-TRAFFIC = dict(source_digest="779ffd4e50d94a56", fetch_bytes=187892 * 2 * 1024,
+TRAFFIC = dict(source_digest="230317ac9be02fbb", fetch_bytes=187891 * 2 * 1024,
                write_bytes=49088 * 1024)
 
 

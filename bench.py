@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--tail", choices=("fused", "calls"), default="fused",
                     help="fused: the shared expert and combine+norm+upproj as one "
                          "moetail_tail call; calls: as its two entry points")
+    ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
+                    help="tiled: the projections read weights packed once by "
+                         "moetail_pack_weights; rows: row-major weights")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the finalize on a side stream beside the shared expert; "
                          "1: the three calls in order on one stream")
@@ -111,10 +114,14 @@ def main():
         ep = workloads.ep_finalize(s, b=B, K=K, P=P, tp=TP)
         up = workloads.upproj(s, b=B, tp=TP, L=P, N=H)
         sh = workloads.shared(s, b=B, H=H, I=I)
+        # the weights as the projections read them: row-major, or packed
+        # once (at load time, outside every timed region) into the tiled
+        # layout
+        wl = (lambda a: mt.pack_weights(dev(a))) if args.weights == "tiled" else dev
         d = dict(rows=dev(ep["rows"]), idx=dev(ep["idx"]), w=dev(ep["w32"]),
-                 gamma=dev(ep["gamma"]), x=dev(sh["x"]), wg=dev(sh["w_gate"]),
-                 wu=dev(sh["w_up"]), wd=dev(sh["w_down"]), lgamma=dev(up["gamma"]),
-                 w_up=dev(up["w_up"]),
+                 gamma=dev(ep["gamma"]), x=dev(sh["x"]), wg=wl(sh["w_gate"]),
+                 wu=wl(sh["w_up"]), wd=wl(sh["w_down"]), lgamma=dev(up["gamma"]),
+                 w_up=wl(up["w_up"]),
                  lat=torch.empty((TP, B, P), dtype=torch.int16, device="cuda"),
                  rs=torch.empty((B, H), dtype=torch.int16, device="cuda"),
                  out=torch.empty((B, H), dtype=torch.int16, device="cuda"),
@@ -129,16 +136,19 @@ def main():
         mt.moetail_finalize(d["rows"], d["idx"], d["w"], d["gamma"], 1.0, 1e-6, True,
                             partials=d["lat"])
 
+    lay = mt.W_TILED if args.weights == "tiled" else mt.W_ROWS
+
     def shared(d):
-        mt.moetail_shared_expert(d["x"], d["wg"], d["wu"], d["wd"], d["rs"], workspace=d["ws_sh"])
+        mt.moetail_shared_expert(d["x"], d["wg"], d["wu"], d["wd"], d["rs"], workspace=d["ws_sh"],
+                                 w_layout=lay)
 
     def upproj(d):
         mt.moetail_combine_norm_upproj(d["lat"], d["lgamma"], 1e-6, d["w_up"], d["out"],
-                                       rs=d["rs"], workspace=d["ws_up"])
+                                       rs=d["rs"], workspace=d["ws_up"], w_layout=lay)
 
     def tail(d):
         mt.moetail_tail(d["lat"], d["lgamma"], 1e-6, d["w_up"], d["x"], d["wg"], d["wu"], d["wd"],
-                        d["out"], rs=d["rs"], workspace=d["ws_tail"])
+                        d["out"], rs=d["rs"], workspace=d["ws_tail"], w_layout=lay)
 
     side = torch.cuda.Stream()
 
@@ -233,7 +243,7 @@ def main():
     kernels = None
     if not args.no_kernels:
         log("per-config kernel timings")
-        kernels = config_kernels(sets[0], log)
+        kernels = config_kernels(sets[0], log, lay)
 
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
@@ -268,6 +278,7 @@ def main():
                                "projection 3584->7168 (+rs)",
                    "b": B, "P": P, "tp": TP, "K": K, "H": H, "I": I,
                    "global_batch": B, "tail": args.tail, "streams": args.streams,
+                   "weights": args.weights,
                    "parallelism": "one GPU, tp rank partials resident"},
         "gpu_ms_per_step_events": round(gpu_ms, 5),
         "step_algorithmic_bytes": step_bytes,
@@ -301,7 +312,7 @@ def graph_time(fn, reps):
     return a.elapsed_time(b) * 1e3 / reps
 
 
-def config_kernels(base, log):
+def config_kernels(base, log, lay):
     """Per-config timings on cold inputs: enough distinct input sets rotate
     that their total exceeds twice the 256 MB Infinity Cache."""
     import numpy as np
@@ -375,26 +386,29 @@ def config_kernels(base, log):
     del kp
 
     # latent combine + norm + up projection, b in {1, 8, 32, 64}
-    wups = [randn_bf16((H, P), 0.02) for _ in range(12)]
+    def wl(t):
+        return mt.pack_weights(t) if lay == mt.W_TILED else t
+
+    wups = [wl(randn_bf16((H, P), 0.02)) for _ in range(12)]
     for b in (1, 8, 32, 64):
         lat = randn_bf16((TP, b, P), 1.0)
         o = torch.empty((b, H), dtype=torch.int16, device="cuda")
         ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, P, H, TP)
         us = timed(lambda i: mt.moetail_combine_norm_upproj(lat, base["lgamma"], 1e-6, wups[i], o,
-                                                            workspace=ws), 12)
+                                                            workspace=ws, w_layout=lay), 12)
         add(f"combine_norm_upproj b={b}", us, H * P * 2 + TP * b * P * 2 + P * 2 + b * H * 2,
             weight_roofline_us=round(H * P * 2 / HBM_PEAK_GBPS / 1e3, 2))
     del wups
 
     # shared expert, b in {16, 32, 64, 128}
-    ws_sets = [(randn_bf16((I, H), 0.02), randn_bf16((I, H), 0.02), randn_bf16((H, I), 0.02))
-               for _ in range(2)]
+    ws_sets = [(wl(randn_bf16((I, H), 0.02)), wl(randn_bf16((I, H), 0.02)),
+                wl(randn_bf16((H, I), 0.02))) for _ in range(2)]
     for b in (16, 32, 64, 128):
         x = randn_bf16((b, H), 1.0)
         rs = torch.empty((b, H), dtype=torch.int16, device="cuda")
         ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
-        us = timed(lambda i: mt.moetail_shared_expert(x, *ws_sets[i], rs, workspace=ws), 2,
-                   reps=12)
+        us = timed(lambda i: mt.moetail_shared_expert(x, *ws_sets[i], rs, workspace=ws,
+                                                      w_layout=lay), 2, reps=12)
         add(f"shared_expert b={b}", us, 3 * H * I * 2 + 2 * b * H * 2,
             weight_roofline_us=round(3 * H * I * 2 / HBM_PEAK_GBPS / 1e3, 2))
     return res

@@ -24,9 +24,10 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 NORM_GAIN_AFTER, NORM_GAIN_FIRST, NO_NORM = 0, 1, 2  # moetail_finalize norm modes
 OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL = 0, 1, 2, 3, 4
+W_ROWS, W_TILED = 0, 1  # weight layouts of the projections
 
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-          "moetail_shared_expert", "moetail_tail")
+          "moetail_shared_expert", "moetail_tail", "moetail_pack_weights")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string")
 
 
@@ -53,11 +54,12 @@ def lib() -> ctypes.CDLL:
                                        P, P, P]
         L.moetail_tp_finalize.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, I32, I32, I32,
                                           P, P, SZ, P]
-        L.moetail_combine_norm_upproj.argtypes = [P, I32, P, F, P, I32, P, I32, I32, P, P, P,
-                                                  SZ, P]
-        L.moetail_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, P, SZ, P]
+        L.moetail_combine_norm_upproj.argtypes = [P, I32, P, F, P, I32, P, I32, I32, P, P, I32,
+                                                  P, SZ, P]
+        L.moetail_shared_expert.argtypes = [P, I32, I32, P, P, I32, P, P, P, I32, P, SZ, P]
         L.moetail_tail.argtypes = [P, I32, P, F, P, I32, P, P, P, P, I32, I32, I32, P, P, P, P,
-                                   P, SZ, P]
+                                   I32, P, SZ, P]
+        L.moetail_pack_weights.argtypes = [P, I64, I32, P, P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
@@ -150,11 +152,11 @@ def moetail_tp_finalize(kpartials, permuted_idx, route_w, gamma, gain_center, ep
 
 
 def moetail_combine_norm_upproj(latent_partials, gamma, eps, w_up, out, rs=None, normed=None,
-                                workspace=None, stream=None):
-    """latent_partials [tp, b, L], gamma [L], w_up [N, L], rs [b, N] or None;
-    writes out [b, N] and normed [b, L] when given.  workspace: a device
-    tensor of at least workspace_bytes(OP_COMBINE_NORM_UPPROJ, b, L, N, tp)
-    bytes."""
+                                workspace=None, stream=None, w_layout=W_ROWS):
+    """latent_partials [tp, b, L], gamma [L], w_up [N, L] (row-major, or its
+    pack_weights copy with w_layout=W_TILED), rs [b, N] or None; writes out
+    [b, N] and normed [b, L] when given.  workspace: a device tensor of at
+    least workspace_bytes(OP_COMBINE_NORM_UPPROJ, b, L, N, tp) bytes."""
     for t, n in ((latent_partials, "latent_partials"), (gamma, "gamma"), (w_up, "w_up"),
                  (out, "out"), (rs, "rs"), (normed, "normed")):
         _bf16(t, n)
@@ -164,12 +166,14 @@ def moetail_combine_norm_upproj(latent_partials, gamma, eps, w_up, out, rs=None,
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().moetail_combine_norm_upproj(_ptr(latent_partials), tp, _ptr(gamma), float(eps),
                                            _ptr(w_up), N, _ptr(rs), b, L, _ptr(normed),
-                                           _ptr(out), ws, wsb, _stream(stream))
+                                           _ptr(out), int(w_layout), ws, wsb, _stream(stream))
     _check(st, "moetail_combine_norm_upproj")
 
 
-def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, stream=None):
-    """x [b, H], w_gate/w_up [I, H], w_down [H, I]; writes rs [b, H] and h
+def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, stream=None,
+                          w_layout=W_ROWS):
+    """x [b, H], w_gate/w_up [I, H], w_down [H, I] (all row-major, or all
+    pack_weights copies with w_layout=W_TILED); writes rs [b, H] and h
     [b, I] when given.  workspace: at least
     workspace_bytes(OP_SHARED_EXPERT, b, H, I) bytes."""
     for t, n in ((x, "x"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"), (rs, "rs"),
@@ -180,17 +184,18 @@ def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, s
     ws = _ptr(workspace) if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().moetail_shared_expert(_ptr(x), b, H, _ptr(w_gate), _ptr(w_up), I, _ptr(w_down),
-                                     _ptr(h), _ptr(rs), ws, wsb, _stream(stream))
+                                     _ptr(h), _ptr(rs), int(w_layout), ws, wsb, _stream(stream))
     _check(st, "moetail_shared_expert")
 
 
 def moetail_tail(latent_partials, gamma, eps, w_up, x, w_gate, w_up_shared, w_down, out,
-                 rs=None, normed=None, h=None, workspace=None, stream=None):
+                 rs=None, normed=None, h=None, workspace=None, stream=None, w_layout=W_ROWS):
     """The tail after the finalize in one call: rs = shared expert of x,
     out = up projection of the normed rank-combined latent + rs.
     latent_partials [tp, b, L], gamma [L], w_up [H, L]; x [b, H], w_gate and
     w_up_shared [I, H], w_down [H, I]; writes out [b, H] and rs [b, H],
-    normed [b, L], h [b, I] when given.  workspace: at least
+    normed [b, L], h [b, I] when given.  The four weights are all row-major,
+    or all pack_weights copies with w_layout=W_TILED.  workspace: at least
     workspace_bytes(OP_TAIL, b, L, H, I) bytes."""
     for t, n in ((latent_partials, "latent_partials"), (gamma, "gamma"), (w_up, "w_up"),
                  (x, "x"), (w_gate, "w_gate"), (w_up_shared, "w_up_shared"), (w_down, "w_down"),
@@ -203,9 +208,27 @@ def moetail_tail(latent_partials, gamma, eps, w_up, x, w_gate, w_up_shared, w_do
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().moetail_tail(_ptr(latent_partials), tp, _ptr(gamma), float(eps), _ptr(w_up), L,
                             _ptr(x), _ptr(w_gate), _ptr(w_up_shared), _ptr(w_down), H, I, b,
-                            _ptr(out), _ptr(rs), _ptr(normed), _ptr(h), ws, wsb,
-                            _stream(stream))
+                            _ptr(out), _ptr(rs), _ptr(normed), _ptr(h), int(w_layout), ws,
+                            wsb, _stream(stream))
     _check(st, "moetail_tail")
+
+
+def moetail_pack_weights(w, packed, stream=None):
+    """packed (same shape and size as w [n, k]) = the tiled copy of the
+    row-major weight matrix w, for the projections' w_layout=W_TILED."""
+    _bf16(w, "w"), _bf16(packed, "packed")
+    if w.dim() != 2 or packed.numel() != w.numel():
+        raise ValueError("w must be [n, k] and packed the same size")
+    n, k = w.shape
+    st = lib().moetail_pack_weights(_ptr(w), n, k, _ptr(packed), _stream(stream))
+    _check(st, "moetail_pack_weights")
+
+
+def pack_weights(w, stream=None):
+    """A new tensor shaped like w holding its tiled copy."""
+    packed = torch.empty_like(w)
+    moetail_pack_weights(w, packed, stream=stream)
+    return packed
 
 
 def new_workspace(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0, device="cuda"):

@@ -36,6 +36,10 @@ int check_norm_args(const void* w, int w_dtype, const uint16_t* gamma, float eps
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOETAIL_OK : MOETAIL_EHIP; }
 
+bool layout_ok(int w_layout) {
+  return w_layout == MOETAIL_W_ROWS || w_layout == MOETAIL_W_TILED;
+}
+
 // The library's projection plans, with optional overrides read from the
 // environment at every call (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES,
 // _BLOCKS, _MR and _PF for KIND in UPPROJ, GATEUP, DOWN.  An override that
@@ -156,10 +160,10 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32
 
 int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
                                 float eps, const uint16_t* w_up, int N, const uint16_t* rs, int b,
-                                int L, uint16_t* normed, uint16_t* out, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                int L, uint16_t* normed, uint16_t* out, int w_layout,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
-  if (b < 0 || tp <= 0 || N <= 0 || L <= 0) return MOETAIL_EINVAL;
+  if (b < 0 || tp <= 0 || N <= 0 || L <= 0 || !layout_ok(w_layout)) return MOETAIL_EINVAL;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
   if (!a16(latent_partials) || !a16(gamma) || !a16(w_up) || !a16(out)) return MOETAIL_EINVAL;
   if ((rs && !a16(rs)) || (normed && !a16(normed))) return MOETAIL_EINVAL;
@@ -175,16 +179,16 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const u
   uint16_t* y = normed ? normed : reinterpret_cast<uint16_t*>(ws);
   float* part = lay.part_bytes ? reinterpret_cast<float*>(ws + (normed ? 0 : lay.y_bytes)) : nullptr;
   hipError_t e = launch_latent_norm(latent_partials, tp, b, L, gamma, eps, y, stream);
-  if (e == hipSuccess) e = launch_linear(w_up, N, L, y, b, rs, out, lay.plan, part, stream);
+  if (e == hipSuccess) e = launch_linear(w_up, w_layout, N, L, y, b, rs, out, lay.plan, part, stream);
   return hip_status(e);
 }
 
 int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gate,
                           const uint16_t* w_upw, int I, const uint16_t* w_down, uint16_t* h,
-                          uint16_t* rs, void* workspace, size_t workspace_bytes,
+                          uint16_t* rs, int w_layout, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
-  if (b < 0 || H <= 0 || I <= 0) return MOETAIL_EINVAL;
+  if (b < 0 || H <= 0 || I <= 0 || !layout_ok(w_layout)) return MOETAIL_EINVAL;
   if (!a16(x) || !a16(w_gate) || !a16(w_upw) || !a16(w_down) || !a16(rs)) return MOETAIL_EINVAL;
   if (h && !a16(h)) return MOETAIL_EINVAL;
   if (H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
@@ -198,18 +202,21 @@ int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gat
   char* ws = static_cast<char*>(workspace);
   uint16_t* hb = h ? h : reinterpret_cast<uint16_t*>(ws);
   float* part = lay.part_bytes ? reinterpret_cast<float*>(ws + (h ? 0 : lay.h_bytes)) : nullptr;
-  hipError_t e = launch_gate_up(w_gate, w_upw, I, H, x, b, hb, lay.gate_up, part, stream);
-  if (e == hipSuccess) e = launch_linear(w_down, H, I, hb, b, nullptr, rs, lay.down, part, stream);
+  hipError_t e =
+      launch_gate_up(w_gate, w_upw, w_layout, I, H, x, b, hb, lay.gate_up, part, stream);
+  if (e == hipSuccess)
+    e = launch_linear(w_down, w_layout, H, I, hb, b, nullptr, rs, lay.down, part, stream);
   return hip_status(e);
 }
 
 int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
                  const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
                  const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
-                 uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h, int w_layout,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (b == 0) return MOETAIL_OK;
-  if (b < 0 || tp <= 0 || L <= 0 || H <= 0 || I <= 0) return MOETAIL_EINVAL;
+  if (b < 0 || tp <= 0 || L <= 0 || H <= 0 || I <= 0 || !layout_ok(w_layout))
+    return MOETAIL_EINVAL;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
   if (!a16(latent_partials) || !a16(gamma) || !a16(w_up) || !a16(x) || !a16(w_gate) ||
       !a16(w_upw) || !a16(w_down) || !a16(out))
@@ -235,8 +242,19 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
     ws += lay.y_bytes;
   }
   TailArgs a{x, w_gate, w_upw, w_down, H, I, latent_partials, tp, gamma, eps, w_up, L, b, hb, yb,
-             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes};
+             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout};
   return hip_status(launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream));
+}
+
+int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
+                         hipStream_t stream) {
+  if (n == 0) return MOETAIL_OK;
+  if (n < 0 || k <= 0 || !a16(w) || !a16(packed)) return MOETAIL_EINVAL;
+  if (n % 16 || k % 32) return MOETAIL_EUNSUPPORTED;
+  const uintptr_t bytes = (uintptr_t)n * (uintptr_t)k * sizeof(uint16_t);
+  const uintptr_t wi = reinterpret_cast<uintptr_t>(w), pi = reinterpret_cast<uintptr_t>(packed);
+  if (wi < pi + bytes && pi < wi + bytes) return MOETAIL_EINVAL;  // overlapping
+  return hip_status(launch_pack_weights(w, n, k, packed, stream));
 }
 
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {

@@ -107,18 +107,23 @@ struct TailArgs {
   uint16_t* out;            // [b][H]
   float* partials;          // gate/up partials, then down and up partials
   size_t down_part_bytes;   // offset of the up partials
+  int tiled;                // the four weights in the tiled layout
 };
 hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
                        const ProjPlan& up, const GroupPlan& g, hipStream_t stream);
 
-// out[b][N] = bf16(W[N][K] . X[b][K] + rs), -0 as +0.
-hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X,
+// The tiled copy of a [n][k] weight matrix (n % 16 == 0, k % 32 == 0).
+hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
+                               hipStream_t stream);
+
+// out[b][N] = bf16(W[N][K] . X[b][K] + rs), -0 as +0; tiled: W's layout.
+hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint16_t* X,
                          int b, const uint16_t* rs, uint16_t* out,
                          const ProjPlan& plan, float* partials,
                          hipStream_t stream);
 
 // h[b][I] = bf16(silu(bf16(Wg . x)) * bf16(Wu . x)), -0 as +0.
-hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int I, int H,
+hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
                           const uint16_t* X, int b, uint16_t* h,
                           const ProjPlan& plan, float* partials,
                           hipStream_t stream);

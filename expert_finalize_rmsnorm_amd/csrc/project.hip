@@ -51,6 +51,7 @@ struct FxArgs {
                        // direct epilogue
   const uint16_t* rs;  // direct epilogue only: [b][N] or null
   uint16_t* out;       // direct epilogue only: [b][N]
+  int tiled;           // weights in the tiled layout (moetail_pack_weights)
 };
 
 __device__ __forceinline__ float silu(float z) {
@@ -102,12 +103,21 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // wave-uniform
   const int total = my_units * nsteps;
 
+  // Where this lane's 8 weights of a k step lie.  Row-major: row lrow of
+  // the tile, columns 8 kq.. of the step (16 rows x 64 B per wave load).
+  // Tiled: the step's 16 x 32 fragment is 1 KB in the accumulator's operand
+  // order, lane l at 16 l bytes (one contiguous 1 KB per wave load).  A
+  // 16-row tile starts 16 K elements further in both layouts.
+  const int64_t lane_off = a.tiled ? 8 * lane : (int64_t)lrow * K + 8 * kq;
+  const int k_mul = a.tiled ? 16 : 1;        // elements per k of a slice start
+  const int step_stride = a.tiled ? 512 : kKStep;
+
   // The MR tiles of a unit lie in one matrix (n0 % (16 * MR) == 0).
   auto unit_ptr = [&](int unit) {
     const int row0 = unit * 16 * MR;
     const uint16_t* base = row0 < a.n0 ? a.A0 + (int64_t)row0 * K
                                        : a.A1 + (int64_t)(row0 - a.n0) * K;
-    return base + (int64_t)lrow * K + kb + 8 * kq;
+    return base + lane_off + (int64_t)kb * k_mul;
   };
 
   // Load cursor: (unit, step); past the wave's last step it stays on it
@@ -116,7 +126,7 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   const uint16_t* l_ptr = total > 0 ? unit_ptr(u) : a.A0;
   auto next_load = [&](uint4 (&q)[MR]) {
 #pragma unroll
-    for (int m = 0; m < MR; ++m) q[m] = load16(l_ptr + (int64_t)m * 16 * K + l_step * kKStep);
+    for (int m = 0; m < MR; ++m) q[m] = load16(l_ptr + (int64_t)m * 16 * K + l_step * step_stride);
     if (l_left > 1) {
       --l_left;
       if (++l_step == nsteps) {
@@ -387,6 +397,24 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
   *reinterpret_cast<uint2*>(out + (int64_t)tok * N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
 }
 
+// Tiled weight layout: fragment (t, s) of a [N][K] matrix -- rows
+// 16 t .. 16 t + 15, columns 32 s .. 32 s + 31 -- is 1 KB at element
+// (t * K/32 + s) * 512, lane l's 8 values (row 16 t + l % 16, columns
+// 32 s + 8 (l / 16) ..) at element 8 l of it: the operand order of
+// v_mfma_f32_16x16x32_bf16.  One thread per 16 bytes of the result.
+__global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* w, int64_t n, int k,
+                                                          uint16_t* packed) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t pieces = n * k / 8;
+  if (i >= pieces) return;
+  const int64_t f = i >> 6;
+  const int l = (int)(i & 63);
+  const int steps = k / kKStep;
+  const int64_t t = f / steps;
+  const int st = (int)(f - t * steps);
+  store16(packed + i * 8, load16(w + (16 * t + (l & 15)) * k + kKStep * st + 8 * (l >> 4)));
+}
+
 int token_blocks(int b) {
   const int nt = (b + 15) / 16;
   return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : 8;
@@ -608,7 +636,7 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
                                                 a.down_part_bytes);
   // 1. gate/up partials
   FxArgs gu{a.w_gate, a.w_upw, a.I, 2 * a.I, a.H, a.x, b, gate_up.k_per_split,
-            gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr};
+            gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr, a.tiled};
   hipError_t e = fx_dispatch(gu, gate_up, s);
   if (e != hipSuccess) return e;
   // 2. h from the gate/up partials, beside y from the latent partials
@@ -623,9 +651,9 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   if (e != hipSuccess) return e;
   // 3. down and up projections in one grid (the gate/up partials are consumed)
   FxArgs dn{a.w_down, nullptr, a.H, a.H, a.I, a.h, b, down.k_per_split, g.bps0, down.pitch,
-            part, nullptr, nullptr};
+            part, nullptr, nullptr, a.tiled};
   FxArgs upa{a.w_up, nullptr, a.H, a.H, a.L, a.y, b, up.k_per_split, g.bps1, up.pitch, up_part,
-             nullptr, nullptr};
+             nullptr, nullptr, a.tiled};
   const int blocks0 = g.bps0 * down.splits;
   const int blocks = blocks0 + g.bps1 * up.splits;
   const size_t lds = down.lds > up.lds ? down.lds : up.lds;
@@ -645,13 +673,21 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   return hipGetLastError();
 }
 
-hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X, int b,
+hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
+                               hipStream_t s) {
+  const int64_t pieces = n * k / 8;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
+                     w, n, k, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint16_t* X, int b,
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
   const bool split = plan.splits > 1;
   f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
-           split ? part : nullptr, rs, out};
+           split ? part : nullptr, rs, out, tiled};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess || !split) return e;
   const int ntb = token_blocks(b);
@@ -661,13 +697,13 @@ hipError_t launch_linear(const uint16_t* W, int N, int K, const uint16_t* X, int
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int I, int H, const uint16_t* X,
-                          int b, uint16_t* h, const ProjPlan& plan, float* partials,
-                          hipStream_t s) {
+hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
+                          const uint16_t* X, int b, uint16_t* h, const ProjPlan& plan,
+                          float* partials, hipStream_t s) {
   // Gate rows [0, I) and up rows [I, 2I) in one grid; SiLU in the reduction.
   f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{Wg, Wu, I, 2 * I, H, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
-           part, nullptr, nullptr};
+           part, nullptr, nullptr, tiled};
   hipError_t e = fx_dispatch(a, plan, s);
   if (e != hipSuccess) return e;
   const int ntb = token_blocks(b);

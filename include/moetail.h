@@ -57,6 +57,10 @@ extern "C" {
 #define MOETAIL_NORM_GAIN_FIRST 1 /* weight_before_norm: s = x * g, n = s * inv */
 #define MOETAIL_NO_NORM 2         /* [tail_runtime] Kimi finalize: n = x */
 
+/* Weight layouts of the projections (their w_layout argument). */
+#define MOETAIL_W_ROWS 0  /* dense row-major [N][K]: row n makes output column n */
+#define MOETAIL_W_TILED 1 /* the tiled copy moetail_pack_weights makes */
+
 /* Operation ids for moetail_workspace_bytes. */
 #define MOETAIL_OP_FINALIZE 0
 #define MOETAIL_OP_TP_FINALIZE 1
@@ -152,6 +156,7 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,
  *   rs              [b][N] BF16 shared-expert reduce-scatter partial, or NULL.
  *   normed          [b][L] BF16 written (y), or NULL.
  *   out             [b][N] BF16 written.
+ *   w_layout        MOETAIL_W_ROWS or MOETAIL_W_TILED: the layout of w_up.
  *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_COMBINE_NORM_UPPROJ,
  *                   b, L, N, tp) bytes of device memory, 256-byte aligned.
  *   Limits: b <= 128, 1 <= tp <= 32, 32 <= L <= 8192, L % 32 == 0,
@@ -161,7 +166,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp,
                                 const uint16_t* gamma, float eps,
                                 const uint16_t* w_up, int N,
                                 const uint16_t* rs, int b, int L,
-                                uint16_t* normed, uint16_t* out,
+                                uint16_t* normed, uint16_t* out, int w_layout,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
@@ -177,6 +182,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp,
  *           tensor passes p and p + I*H).   w_down [H][I] BF16.
  *   h       [b][I] BF16 written, or NULL.
  *   rs      [b][H] BF16 written (the input of moetail_combine_norm_upproj).
+ *   w_layout MOETAIL_W_ROWS or MOETAIL_W_TILED: the layout of the three weights.
  *   workspace at least moetail_workspace_bytes(MOETAIL_OP_SHARED_EXPERT,
  *           b, H, I, 0) bytes, 256-byte aligned.
  *   Limits: b <= 128, H % 64 == 0, I % 64 == 0, 64 <= H, I <= MOETAIL_MAX_GEMM_K.
@@ -184,7 +190,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp,
 int moetail_shared_expert(const uint16_t* x, int b, int H,
                           const uint16_t* w_gate, const uint16_t* w_upw, int I,
                           const uint16_t* w_down, uint16_t* h, uint16_t* rs,
-                          void* workspace, size_t workspace_bytes,
+                          int w_layout, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
 /*
@@ -205,6 +211,8 @@ int moetail_shared_expert(const uint16_t* x, int b, int H,
  *   out             [b][H] BF16 written.
  *   rs, normed, h   [b][H], [b][L], [b][I] BF16 written, or NULL (then kept
  *                   in the workspace or not kept).
+ *   w_layout        MOETAIL_W_ROWS or MOETAIL_W_TILED: the layout of all four
+ *                   weights.
  *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_TAIL, b, L,
  *                   H, I) bytes, 256-byte aligned.
  *   Limits: those of the two calls: b <= 128, 1 <= tp <= 32, L % 32 == 0,
@@ -214,8 +222,30 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
                  float eps, const uint16_t* w_up, int L, const uint16_t* x,
                  const uint16_t* w_gate, const uint16_t* w_upw,
                  const uint16_t* w_down, int H, int I, int b, uint16_t* out,
-                 uint16_t* rs, uint16_t* normed, uint16_t* h, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream);
+                 uint16_t* rs, uint16_t* normed, uint16_t* h, int w_layout,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The tiled copy of a weight matrix, made once when the weights are loaded
+ * (weights are static at decode time).  The projections read either layout
+ * (their w_layout argument) and give the same bits from both; the tiled one
+ * lets every wave-wide weight load read 1 KB of contiguous memory instead
+ * of 64 bytes of each of 16 rows (measured on MI355X: 5.9 against 4.4 TB/s
+ * for a weight stream).  Not on the pages: their kernels read row-major
+ * weights through TMA into swizzled shared memory.
+ *     packed[((t * k/32) + s) * 512 + 8 l + e]
+ *         = w[(16 t + l % 16) * k + 32 s + 8 (l / 16) + e]
+ * for every 16-row tile t, 32-column step s, lane l < 64 and e < 8: each
+ * 16 x 32 block is 1 KB in the operand order of the MFMA that reads it.  A
+ * stacked [2I][H] gate/up matrix packs as one [2I][H] matrix (the up half
+ * starts I*H elements in, as in the row-major layout).
+ *
+ *   w       [n][k] BF16 row-major.   packed [n][k] elements BF16, written;
+ *           it may not overlap w.
+ *   Limits: n % 16 == 0, k % 32 == 0 (EUNSUPPORTED otherwise); n == 0 is OK.
+ */
+int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
+                         hipStream_t stream);
 
 /*
  * Workspace bytes an operation needs (0 when none):

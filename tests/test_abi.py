@@ -30,8 +30,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-              "moetail_shared_expert", "moetail_tail", "moetail_workspace_bytes",
-              "moetail_status_string"):
+              "moetail_shared_expert", "moetail_tail", "moetail_pack_weights",
+              "moetail_workspace_bytes", "moetail_status_string"):
         assert n in names
     assert set(names) == set(mt.ENTRY_POINTS)
 
@@ -117,11 +117,11 @@ def test_tp_finalize_validation():
 
 def _up(ws=A, wsb=1 << 30, **kw):
     a = dict(lat=A, tp=8, gamma=A, eps=1e-6, w=A, N=7168, rs=None, b=32, L=3584, normed=None,
-             out=A)
+             out=A, lay=mt.W_ROWS)
     a.update(kw)
     return mt.lib().moetail_combine_norm_upproj(a["lat"], a["tp"], a["gamma"], a["eps"], a["w"],
                                                 a["N"], a["rs"], a["b"], a["L"], a["normed"],
-                                                a["out"], ws, wsb, None)
+                                                a["out"], a["lay"], ws, wsb, None)
 
 
 def test_upproj_validation():
@@ -135,13 +135,16 @@ def test_upproj_validation():
     assert _up(ws=None, wsb=0) == mt.EWORKSPACE  # y needs a home when normed is NULL
     assert _up(wsb=16) == mt.EWORKSPACE
     assert _up(ws=A + 16) == mt.EWORKSPACE  # 256-byte alignment
+    assert _up(lay=2) == mt.EINVAL
+    assert _up(lay=-1) == mt.EINVAL
+    assert _up(lay=2, b=0) == mt.OK
 
 
 def _sh(ws=A, wsb=1 << 30, **kw):
-    a = dict(x=A, b=32, H=7168, wg=A, wu=A, I=6144, wd=A, h=None, rs=A)
+    a = dict(x=A, b=32, H=7168, wg=A, wu=A, I=6144, wd=A, h=None, rs=A, lay=mt.W_TILED)
     a.update(kw)
     return mt.lib().moetail_shared_expert(a["x"], a["b"], a["H"], a["wg"], a["wu"], a["I"],
-                                          a["wd"], a["h"], a["rs"], ws, wsb, None)
+                                          a["wd"], a["h"], a["rs"], a["lay"], ws, wsb, None)
 
 
 def test_shared_validation():
@@ -154,15 +157,16 @@ def test_shared_validation():
     assert _sh(I=6100) == mt.EUNSUPPORTED
     assert _sh(b=200) == mt.EUNSUPPORTED
     assert _sh(ws=None, wsb=0) == mt.EWORKSPACE
+    assert _sh(lay=5) == mt.EINVAL
 
 
 def _tail(ws=A, wsb=1 << 31, **kw):
     a = dict(lat=A, tp=8, gamma=A, eps=1e-6, wup=A, L=3584, x=A, wg=A, wu=A, wd=A, H=7168,
-             I=6144, b=64, out=A, rs=None, normed=None, h=None)
+             I=6144, b=64, out=A, rs=None, normed=None, h=None, lay=mt.W_TILED)
     a.update(kw)
     return mt.lib().moetail_tail(a["lat"], a["tp"], a["gamma"], a["eps"], a["wup"], a["L"],
                                  a["x"], a["wg"], a["wu"], a["wd"], a["H"], a["I"], a["b"],
-                                 a["out"], a["rs"], a["normed"], a["h"], ws, wsb, None)
+                                 a["out"], a["rs"], a["normed"], a["h"], a["lay"], ws, wsb, None)
 
 
 def test_finalize_norm_mode_validation():
@@ -196,6 +200,22 @@ def test_tail_validation():
     assert _tail(ws=None, wsb=0) == mt.EWORKSPACE
     assert _tail(wsb=16) == mt.EWORKSPACE
     assert _tail(ws=A + 16) == mt.EWORKSPACE
+    assert _tail(lay=7) == mt.EINVAL
+
+
+def test_pack_weights_validation():
+    lib = mt.lib()
+    assert lib.moetail_pack_weights(A, 0, 7168, A, None) == mt.OK  # nothing to pack
+    assert lib.moetail_pack_weights(None, 16, 32, A, None) == mt.EINVAL
+    assert lib.moetail_pack_weights(A, 16, 32, None, None) == mt.EINVAL
+    assert lib.moetail_pack_weights(A + 8, 16, 32, 1 << 30, None) == mt.EINVAL  # misaligned
+    assert lib.moetail_pack_weights(A, -16, 32, 1 << 30, None) == mt.EINVAL
+    assert lib.moetail_pack_weights(A, 16, 0, 1 << 30, None) == mt.EINVAL
+    assert lib.moetail_pack_weights(A, 24, 32, 1 << 30, None) == mt.EUNSUPPORTED  # n % 16
+    assert lib.moetail_pack_weights(A, 16, 48, 1 << 30, None) == mt.EUNSUPPORTED  # k % 32
+    # the copy may not overlap its source
+    assert lib.moetail_pack_weights(A, 16, 32, A + 512, None) == mt.EINVAL
+    assert lib.moetail_pack_weights(A + 512, 16, 32, A, None) == mt.EINVAL
 
 
 @pytest.mark.parametrize("b", [1, 8, 16, 32, 64, 128])

@@ -266,14 +266,21 @@ def test_tp_golden_round_before_norm():
 
 # ------------------------------------ latent combine + norm + up projection --
 
-def run_upproj(inp, rs=None, with_normed=True):
+def weight(w, layout):
+    """A weight matrix on the device in the given layout."""
+    d = dev(w)
+    return mt.pack_weights(d) if layout == mt.W_TILED else d
+
+
+def run_upproj(inp, rs=None, with_normed=True, layout=mt.W_ROWS):
     b, L, N, tp = inp["b"], inp["L"], inp["N"], inp["tp"]
     out = empty_bf16(b, N)
     normed = empty_bf16(b, L) if with_normed else None
     ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L, N, tp)
     mt.moetail_combine_norm_upproj(dev(inp["lat"]), dev(inp["gamma"]), inp["eps"],
-                                   dev(inp["w_up"]), out, rs=None if rs is None else dev(rs),
-                                   normed=normed, workspace=ws)
+                                   weight(inp["w_up"], layout), out,
+                                   rs=None if rs is None else dev(rs), normed=normed,
+                                   workspace=ws, w_layout=layout)
     return (host(normed) if normed is not None else None), host(out)
 
 
@@ -329,13 +336,14 @@ def test_upproj_unit_rows_and_zero_weights():
 
 # ----------------------------------------------------------- shared expert --
 
-def run_shared(inp, with_h=True):
+def run_shared(inp, with_h=True, layout=mt.W_ROWS):
     b, H, I = inp["b"], inp["H"], inp["I"]
     rs = empty_bf16(b, H)
     h = empty_bf16(b, I) if with_h else None
     ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
-    mt.moetail_shared_expert(dev(inp["x"]), dev(inp["w_gate"]), dev(inp["w_up"]),
-                             dev(inp["w_down"]), rs, h=h, workspace=ws)
+    mt.moetail_shared_expert(dev(inp["x"]), weight(inp["w_gate"], layout),
+                             weight(inp["w_up"], layout), weight(inp["w_down"], layout), rs, h=h,
+                             workspace=ws, w_layout=layout)
     return (host(h) if h is not None else None), host(rs)
 
 
@@ -419,6 +427,10 @@ def test_projection_plan_overrides(b, monkeypatch):
         got_h, got_rs = run_shared(sh)
         gemm_bar(got_h, want_h, f"h b={b} {ov}")
         gemm_bar(got_rs, want_rs, f"rs b={b} {ov}")
+        # the tiled weight layout: the same bits in every kernel shape
+        assert np.array_equal(run_upproj(up, rs=up["rs"], layout=mt.W_TILED)[1], got_up)
+        got_h2, got_rs2 = run_shared(sh, layout=mt.W_TILED)
+        assert np.array_equal(got_h2, got_h) and np.array_equal(got_rs2, got_rs)
 
 
 def test_projections_graph_replay():
@@ -523,22 +535,30 @@ def test_tail_step_two_stream_graph_matches_eager():
 
 # ------------------------------------------------------------- fused tail --
 
-def run_tail_and_calls(up, sh, with_opt=True):
-    """moetail_tail, and the two calls it stands for, on the same inputs."""
+def run_tail_and_calls(up, sh, with_opt=True, layout=mt.W_ROWS, calls_layout=None):
+    """moetail_tail (weights in `layout`), and the two calls it stands for
+    (weights in `calls_layout`, the same by default), on the same inputs."""
     b, H, I, L, tp = sh["b"], sh["H"], sh["I"], up["L"], up["tp"]
-    lat, gamma, w_up = dev(up["lat"]), dev(up["gamma"]), dev(up["w_up"])
-    x, wg, wu, wd = dev(sh["x"]), dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"])
+    lat, gamma = dev(up["lat"]), dev(up["gamma"])
+    x = dev(sh["x"])
+    w_up, wg, wu, wd = (weight(up["w_up"], layout), weight(sh["w_gate"], layout),
+                        weight(sh["w_up"], layout), weight(sh["w_down"], layout))
     out = empty_bf16(b, H)
     rs, normed, h = ((empty_bf16(b, H), empty_bf16(b, L), empty_bf16(b, I)) if with_opt
                      else (None, None, None))
     mt.moetail_tail(lat, gamma, up["eps"], w_up, x, wg, wu, wd, out, rs=rs, normed=normed, h=h,
-                    workspace=mt.new_workspace(mt.OP_TAIL, b, L, H, I))
+                    workspace=mt.new_workspace(mt.OP_TAIL, b, L, H, I), w_layout=layout)
+    cl = layout if calls_layout is None else calls_layout
+    if cl != layout:
+        w_up, wg, wu, wd = (weight(up["w_up"], cl), weight(sh["w_gate"], cl),
+                            weight(sh["w_up"], cl), weight(sh["w_down"], cl))
     rs2, h2, out2, normed2 = empty_bf16(b, H), empty_bf16(b, I), empty_bf16(b, H), empty_bf16(b, L)
     mt.moetail_shared_expert(x, wg, wu, wd, rs2, h=h2,
-                             workspace=mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I))
+                             workspace=mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I),
+                             w_layout=cl)
     mt.moetail_combine_norm_upproj(lat, gamma, up["eps"], w_up, out2, rs=rs2, normed=normed2,
                                    workspace=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L, H,
-                                                              tp))
+                                                              tp), w_layout=cl)
     fused = dict(out=host(out), rs=host(rs) if rs is not None else None,
                  normed=host(normed) if normed is not None else None,
                  h=host(h) if h is not None else None)
@@ -686,3 +706,55 @@ def test_plain_route_order():
     for mode in ("out", "both"):
         _, got_o = run_plain(inp, mode=mode, gamma=False)
         assert [f"{int(v):04x}" for v in got_o.ravel()] == ["3f80"] * P
+
+
+# ---------------------------------------------------- tiled weight layout --
+
+def tiled_reference(w: np.ndarray) -> np.ndarray:
+    """The tiled layout written out with numpy: block (t, s) of 16 rows and
+    32 columns in MFMA operand order, lane l = r + 16 q holding row 16 t + r,
+    columns 32 s + 8 q .. 32 s + 8 q + 7."""
+    n, k = w.shape
+    return w.reshape(n // 16, 16, k // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(n, k)
+
+
+@pytest.mark.parametrize("n,k", [(16, 32), (48, 96), (192, 1024), (7168, 3584)])
+def test_pack_weights_layout(n, k):
+    w = np.random.default_rng(n + k).integers(0, 1 << 16, (n, k), dtype=np.uint16)
+    got = host(mt.pack_weights(dev(w)))
+    assert np.array_equal(got, tiled_reference(w))
+    # the first fragment, spelled out: lane 17 = row 1, columns 8..15
+    assert np.array_equal(got.reshape(-1)[17 * 8:18 * 8], w[1, 8:16])
+
+
+@pytest.mark.parametrize("b", [1, 32, 64])
+def test_tiled_weights_same_bits_upproj(b):
+    inp = workloads.upproj(40 + b, b=b, with_rs=True)
+    rows = run_upproj(inp, rs=inp["rs"])
+    tiled = run_upproj(inp, rs=inp["rs"], layout=mt.W_TILED)
+    assert np.array_equal(rows[0], tiled[0]) and np.array_equal(rows[1], tiled[1])
+
+
+@pytest.mark.parametrize("b,H,I", [(1, 7168, 6144), (64, 7168, 6144), (128, 1024, 2048),
+                                   (5, 512, 256), (33, 256, 128)])
+def test_tiled_weights_same_bits_shared(b, H, I):
+    inp = workloads.shared(50 + b, b=b, H=H, I=I)
+    h0, rs0 = run_shared(inp)
+    h1, rs1 = run_shared(inp, layout=mt.W_TILED)
+    assert np.array_equal(h0, h1) and np.array_equal(rs0, rs1)
+    if H * I <= 1 << 20:
+        want_h, want_rs = oracle.shared_expert(inp["x"], inp["w_gate"], inp["w_up"],
+                                               inp["w_down"], nthreads=NT)
+        gemm_bar(h1, want_h, "tiled h")
+        gemm_bar(rs1, want_rs, "tiled rs")
+
+
+@pytest.mark.parametrize("b,tp,L,H,I", [(64, 8, 3584, 7168, 6144), (5, 3, 544, 256, 128),
+                                        (128, 2, 1024, 512, 192)])
+def test_tiled_weights_same_bits_tail(b, tp, L, H, I):
+    """The fused tail on tiled weights = the two calls on row-major weights."""
+    up = workloads.upproj(60 + b, b=b, tp=tp, L=L, N=H)
+    sh = workloads.shared(70 + b, b=b, H=H, I=I)
+    fused, calls = run_tail_and_calls(up, sh, layout=mt.W_TILED, calls_layout=mt.W_ROWS)
+    for key in ("out", "rs", "normed", "h"):
+        assert np.array_equal(fused[key], calls[key]), key

@@ -133,7 +133,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
   __shared__ int pair_count;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nwaves = blockDim.x / kWave;
+  const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;  // the block: a wave per 512 columns
   const int t = blockIdx.x;
   const int P = a.P;
   // Every block of token t takes the whole row's sums of squares; only the
@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
   __shared__ float block_ss[kSlots][16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nwaves = blockDim.x / kWave;
+  const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;  // the block: a wave per 512 columns
   const int t = blockIdx.x;
   const int d = blockIdx.y;
   const int P = a.P;
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
 __global__ void __launch_bounds__(256) rank_combine_kernel(const uint16_t* partials, int tp, int b,
                                                            int P, uint16_t* out) {
   const int per_tok = P / kChunk;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // blocks of 256
   if (i >= (int64_t)b * per_tok) return;
   const int t = (int)(i / per_tok);
   const int col = (int)(i - (int64_t)t * per_tok) * kChunk;
@@ -453,7 +453,7 @@ __global__ void __launch_bounds__(256) tp_rank_sum_kernel(const uint16_t* kpart,
                                                           const int32_t* idx, int routes, int P,
                                                           int tp, uint16_t* xr) {
   const int nbk = (P + kBlockCols - 1) / kBlockCols;
-  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // blocks of 4 waves
   if (wid >= (int64_t)routes * nbk) return;
   const int route = (int)(wid / nbk);
   const int j = (int)(wid - (int64_t)route * nbk);

@@ -20,7 +20,7 @@ __device__ __forceinline__ void latent_norm_body(const uint16_t* lat, int tp, in
                                                  int t, float* block_ss) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int nwaves = (L + kBlockCols - 1) / kBlockCols;  // the block: a wave per 512 columns
   const int col = (wave * kWave + lane) * kChunk;
   const bool has = col < L;
   const int colc = has ? col : L - kChunk;

@@ -54,6 +54,14 @@ struct FxArgs {
   int tiled;           // weights in the tiled layout (moetail_pack_weights)
 };
 
+// A block barrier for LDS data only: this thread's LDS writes complete,
+// then s_barrier.  __syncthreads() also makes global memory visible, which
+// waits for every load in flight -- here the weight ring's loads from HBM.
+// The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float silu(float z) {
   const float e = expf(-z);
   const float den = 1.0f + e;
@@ -136,23 +144,46 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
       }
     }
   };
-  uint4 ra[kPF][MR];
-  if (total > 0) {
-#pragma unroll
-    for (int i = 0; i < kPF; ++i) next_load(ra[i]);
-  }
-
   // Stage X[16*NT][kb, ke) in LDS; padded tokens repeat the last real one.
+  // A thread's pieces load in batches of kStage, all issued before the
+  // first LDS store, and the first batch before the weight ring's first
+  // loads: loads complete in issue order, so the activations (L2 hits)
+  // never wait behind a weight load from HBM.
+  constexpr int kStage = 16;
+  constexpr int kThreads = kWave * kWaves;  // (blockDim.x would be a memory load)
   const int cpt = (ke - kb) / 8;  // 16-byte pieces per token
   const int pieces = 16 * NT * cpt;
-  for (int p = threadIdx.x; p < pieces; p += blockDim.x) {
+  auto stage_load = [&](int p) {  // clamped: past the last piece re-reads it
+    p = min(p, pieces - 1);
     const int tok = p / cpt;
     const int pc = p - tok * cpt;
-    const int src = min(tok, a.b - 1);
-    *reinterpret_cast<uint4*>(xs + tok * a.pitch + pc * 8) =
-        load16(a.X + (int64_t)src * K + kb + pc * 8);
+    return load16(a.X + (int64_t)min(tok, a.b - 1) * K + kb + pc * 8);
+  };
+  auto stage_store = [&](int p, const uint4& q) {
+    if (p < pieces) {
+      const int tok = p / cpt;
+      *reinterpret_cast<uint4*>(xs + tok * a.pitch + (p - tok * cpt) * 8) = q;
+    }
+  };
+  uint4 sq[kStage];
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) sq[j] = stage_load(threadIdx.x + j * kThreads);
+
+  // (unconditional: with no work the cursor rests on the matrix's first
+  // element, so the count of loads in flight is the same on every path)
+  uint4 ra[kPF][MR];
+#pragma unroll
+  for (int i = 0; i < kPF; ++i) next_load(ra[i]);
+
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) stage_store(threadIdx.x + j * kThreads, sq[j]);
+  for (int p0 = threadIdx.x + kStage * kThreads; p0 < pieces; p0 += kStage * kThreads) {
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) sq[j] = stage_load(p0 + j * kThreads);
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) stage_store(p0 + j * kThreads, sq[j]);
   }
-  __syncthreads();
+  lds_barrier();
   if (total == 0) return;
 
   f32x4_t acc[MR][NT];
@@ -352,7 +383,7 @@ template <int MODE>
 __global__ void __launch_bounds__(256) split_reduce_kernel(const f32x4_t* partials, int splits,
                                                           int b, int nt_blocks, int N,
                                                           const uint16_t* rs, uint16_t* out) {
-  reduce_body<MODE>((int64_t)blockIdx.x * blockDim.x + threadIdx.x, partials, splits, b,
+  reduce_body<MODE>((int64_t)blockIdx.x * 256 + threadIdx.x, partials, splits, b,
                     nt_blocks, N, rs, out);
 }
 
@@ -367,7 +398,8 @@ __global__ void __launch_bounds__(1024) tail_mid_kernel(const f32x4_t* gu_partia
                                                         float eps, uint16_t* y) {
   __shared__ float block_ss[16];
   if ((int)blockIdx.x < red_blocks) {
-    reduce_body<kGateUp>((int64_t)blockIdx.x * blockDim.x + threadIdx.x, gu_partials, gu_splits,
+    const int threads = kWave * ((L + kBlockCols - 1) / kBlockCols);  // the launch's block
+    reduce_body<kGateUp>((int64_t)blockIdx.x * threads + threadIdx.x, gu_partials, gu_splits,
                          b, nt_blocks, I, nullptr, h);
     return;
   }
@@ -382,7 +414,7 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
                                                       int up_splits, int b, int nt_blocks, int N,
                                                       uint16_t* rs, uint16_t* out) {
   const int64_t per_tile = (int64_t)nt_blocks * kWave;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // blocks of 256
   if (i >= (N / 16) * per_tile) return;
   int tok, r;
   if (!lane_position(i, per_tile, b, tok, r)) return;
@@ -404,7 +436,7 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
 // v_mfma_f32_16x16x32_bf16.  One thread per 16 bytes of the result.
 __global__ void __launch_bounds__(256) pack_weights_kernel(const uint16_t* w, int64_t n, int k,
                                                           uint16_t* packed) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // blocks of 256
   const int64_t pieces = n * k / 8;
   if (i >= pieces) return;
   const int64_t f = i >> 6;

@@ -286,9 +286,29 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   }
 }
 
+// Blocks reach the 8 XCDs in turn (block g on XCD g % 8), and each XCD has
+// its own L2.  The position of block g among the blocks [s, s + m) sorted
+// by (XCD, index): consecutive positions share an XCD, so the blocks of one
+// K slice -- which stage the same activations -- mostly do too.  Only the
+// order in which blocks take their work changes; no sum does.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_position(int g, int s, int m) {
+  auto count = [](int lo, int hi, int y) {  // h in [lo, hi) with h % 8 == y
+    return (hi - y + kXcds - 1) / kXcds - (lo - y + kXcds - 1) / kXcds;
+  };
+  const int x = g % kXcds;
+  int pos = count(s, g, x);
+  for (int y = 0; y < x; ++y) pos += count(s, s + m, y);
+  return pos;
+}
+
+__device__ __forceinline__ int fx_blocks(const FxArgs& a) {
+  return a.blocks_per_slice * ((a.K + a.k_per_split - 1) / a.k_per_split);
+}
+
 template <int NT, int MR, int kPF, int kWaves, int kHold>
 __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
-  px_body<NT, MR, kPF, kWaves, kHold>(a, blockIdx.x);
+  px_body<NT, MR, kPF, kWaves, kHold>(a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
 }
 
 // Two independent projections in one persistent grid (the fused tail's down
@@ -297,9 +317,9 @@ template <int NT, int kWaves, int kHold>
 __global__ void __launch_bounds__(kWave * kWaves) px_group_kernel(FxArgs a0, FxArgs a1,
                                                                   int blocks0) {
   if ((int)blockIdx.x < blocks0)
-    px_body<NT, 1, 8, kWaves, kHold>(a0, blockIdx.x);
+    px_body<NT, 1, 8, kWaves, kHold>(a0, xcd_position(blockIdx.x, 0, blocks0));
   else
-    px_body<NT, 1, 8, kWaves, kHold>(a1, blockIdx.x - blocks0);
+    px_body<NT, 1, 8, kWaves, kHold>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
 }
 
 // Slice partials added in slice order, then the epilogue: one thread per
@@ -475,7 +495,7 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
   double best = 1e300;
   ProjPlan p{};
-  for (int splits = 1; splits <= 64; splits *= 2) {
+  for (int splits = 1; splits <= 64; ++splits) {
     if (t.splits > 0 && splits != t.splits) continue;
     int kps = round_up_i((K + splits - 1) / splits, kKStep);
     if (round_up_i(kps, 128) > kmax) continue;  // slice does not fit the LDS

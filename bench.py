@@ -15,8 +15,8 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
 Steps 2 and 3 run as one moetail_tail call (five launches; --tail calls runs
 them as their two entry points, eight launches: the same bits).
 
-Steps replay HIP graphs of the calls in order on one stream, two steps
-(one per input set) per graph
+Steps replay HIP graphs of the calls in order on one stream, eight steps
+(the two input sets alternating) per graph
 (--streams 2 puts the finalize on a side stream beside the shared expert:
 measured slower, the cross-stream fork and join inside the graph cost more
 than the overlap gains); two input sets (weights and rows) alternate so that the 315 MB of weights per step stream from HBM,
@@ -38,6 +38,7 @@ B, P, TP, K = 64, 3584, 8, 16
 H, I = 7168, 6144
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
+GRAPH_STEPS = 8  # steps per captured graph
 
 
 # HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
@@ -46,7 +47,7 @@ METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
 # scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
 # out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
 # with this digest only.
-TRAFFIC = dict(source_digest="230317ac9be02fbb", fetch_bytes=187891 * 2 * 1024,
+TRAFFIC = dict(source_digest="dd039fff91afb8fb", fetch_bytes=180830 * 2 * 1024,
                write_bytes=49088 * 1024)
 
 
@@ -179,22 +180,23 @@ def main():
     for d in sets:
         step(d)  # eager once before capture
     torch.cuda.synchronize()
-    # One graph holds a step on each input set (two steps per replay: a
-    # decode loop captures many layers' tails in one graph, so the boundary
-    # between replays is shared); an odd step count ends with a one-step graph.
+    # One graph holds GRAPH_STEPS steps, the input sets alternating (a decode
+    # loop captures many layers' tails in one graph, so a replay boundary,
+    # about 8 us of launch, falls once per GRAPH_STEPS steps); the remainder
+    # of a step count runs as one-step graphs.
     cap = torch.cuda.Stream()
-    pair, single = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(pair, stream=cap):
-        for d in sets:
-            step(d)
+    many, single = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(many, stream=cap):
+        for i in range(GRAPH_STEPS):
+            step(sets[i % nsets])
     with torch.cuda.graph(single, stream=cap):
         step(sets[0])
     torch.cuda.synchronize()
 
     def run_steps(n):
-        for _ in range(n // nsets):
-            pair.replay()
-        if n % nsets:
+        for _ in range(n // GRAPH_STEPS):
+            many.replay()
+        for _ in range(n % GRAPH_STEPS):
             single.replay()
 
     log(f"warmup {args.warmup}, timed {args.steps} steps")

@@ -12,15 +12,18 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
   3. the rank-order combine of the 8 partials, RMSNorm, and the 3584 -> 7168
      up projection plus rs -> out [64, 7168] (moetail_combine_norm_upproj).
 
-Steps 2 and 3 run as one moetail_tail call (five launches; --tail calls runs
-them as their two entry points, eight launches: the same bits).
+The step is one moetail_decode_tail call (five launches); --tail fused runs
+it as moetail_finalize then moetail_tail (the same five launches), --tail
+calls as moetail_finalize and the tail's two entry points (eight launches):
+the same bits every way.
 
 Steps replay HIP graphs of the calls in order on one stream, eight steps
 (the two input sets alternating) per graph
-(--streams 2 puts the finalize on a side stream beside the shared expert:
-measured slower, the cross-stream fork and join inside the graph cost more
-than the overlap gains); two input sets (weights and rows) alternate so that the 315 MB of weights per step stream from HBM,
-not from the 256 MB Infinity Cache.  Inputs are resident in HBM before the
+(--tail calls --streams 2 puts the finalize on a side stream beside the
+shared expert: measured slower, the cross-stream fork and join inside the
+graph cost more than the overlap gains); two input sets (weights and rows)
+alternate so that the 315 MB of weights per step stream from HBM, not from
+the 256 MB Infinity Cache.  Inputs are resident in HBM before the
 timed region starts.  Rank 0 prints one JSON line (progress goes to stderr).
 """
 from __future__ import annotations
@@ -86,9 +89,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with two launches of a plain elementwise kernel over 256 MiB "
                          "(reads 256 MiB, writes 256 MiB): the scale for HBM byte counters")
-    ap.add_argument("--tail", choices=("fused", "calls"), default="fused",
-                    help="fused: the shared expert and combine+norm+upproj as one "
-                         "moetail_tail call; calls: as its two entry points")
+    ap.add_argument("--tail", choices=("decode", "fused", "calls"), default="decode",
+                    help="decode: the whole step as one moetail_decode_tail call; "
+                         "fused: moetail_finalize, then the shared expert and "
+                         "combine+norm+upproj as one moetail_tail call; calls: "
+                         "moetail_finalize and the tail's two entry points")
     ap.add_argument("--weights", choices=("tiled", "rows"), default="tiled",
                     help="tiled: the projections read weights packed once by "
                          "moetail_pack_weights; rows: row-major weights")
@@ -153,9 +158,17 @@ def main():
 
     side = torch.cuda.Stream()
 
+    def decode(d):
+        mt.moetail_decode_tail(d["rows"], d["idx"], d["w"], d["gamma"], 1.0, 1e-6, True, d["lat"],
+                               d["lgamma"], 1e-6, d["w_up"], d["x"], d["wg"], d["wu"], d["wd"],
+                               d["out"], rs=d["rs"], workspace=d["ws_tail"], w_layout=lay)
+
     def step(d):
         """finalize runs on a side stream beside the shared expert; the up
         projection waits for both (a fork/join inside the captured graph)."""
+        if args.tail == "decode":
+            decode(d)
+            return
         if args.tail == "fused":
             finalize(d)
             tail(d)

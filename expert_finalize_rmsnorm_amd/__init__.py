@@ -27,7 +27,7 @@ OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL =
 W_ROWS, W_TILED = 0, 1  # weight layouts of the projections
 
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-          "moetail_shared_expert", "moetail_tail", "moetail_pack_weights")
+          "moetail_shared_expert", "moetail_tail", "moetail_decode_tail", "moetail_pack_weights")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string")
 
 
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.moetail_tail.argtypes = [P, I32, P, F, P, I32, P, P, P, P, I32, I32, I32, P, P, P, P,
                                    I32, P, SZ, P]
         L.moetail_pack_weights.argtypes = [P, I64, I32, P, P]
+        L.moetail_decode_tail.argtypes = [P, I64, P, P, I32, P, F, F, I32, I32, P, I32, P, F, P,
+                                          I32, P, P, P, P, I32, I32, I32, P, P, P, P, I32, P, SZ,
+                                          P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
@@ -211,6 +214,37 @@ def moetail_tail(latent_partials, gamma, eps, w_up, x, w_gate, w_up_shared, w_do
                             _ptr(out), _ptr(rs), _ptr(normed), _ptr(h), int(w_layout), ws,
                             wsb, _stream(stream))
     _check(st, "moetail_tail")
+
+
+def moetail_decode_tail(rows, permuted_idx, route_w, fin_gamma, gain_center, fin_eps,
+                        weight_before_norm, latent_partials, gamma, eps, w_up, x, w_gate,
+                        w_up_shared, w_down, out, rs=None, normed=None, h=None, workspace=None,
+                        stream=None, w_layout=W_ROWS):
+    """The whole tail in one call: latent_partials [tp, b, L] = the EP
+    finalize of rows [tp, R, L] (as moetail_finalize with partials only),
+    then out [b, H] = moetail_tail(latent_partials, ...).  workspace: at
+    least workspace_bytes(OP_TAIL, b, L, H, I) bytes."""
+    for t, n in ((rows, "rows"), (fin_gamma, "fin_gamma"), (latent_partials, "latent_partials"),
+                 (gamma, "gamma"), (w_up, "w_up"), (x, "x"), (w_gate, "w_gate"),
+                 (w_up_shared, "w_up_shared"), (w_down, "w_down"), (out, "out"), (rs, "rs"),
+                 (normed, "normed"), (h, "h")):
+        _bf16(t, n)
+    if permuted_idx.dtype != torch.int32:
+        raise TypeError("permuted_idx must be int32")
+    tp, R, L = rows.shape
+    _, b, K = permuted_idx.shape
+    H = x.shape[1]
+    I = w_gate.shape[0]
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().moetail_decode_tail(_ptr(rows), R, _ptr(permuted_idx), _ptr(route_w),
+                                   _weights(route_w), _ptr(fin_gamma), float(gain_center),
+                                   float(fin_eps), int(weight_before_norm), K,
+                                   _ptr(latent_partials), tp, _ptr(gamma), float(eps),
+                                   _ptr(w_up), L, _ptr(x), _ptr(w_gate), _ptr(w_up_shared),
+                                   _ptr(w_down), H, I, b, _ptr(out), _ptr(rs), _ptr(normed),
+                                   _ptr(h), int(w_layout), ws, wsb, _stream(stream))
+    _check(st, "moetail_decode_tail")
 
 
 def moetail_pack_weights(w, packed, stream=None):

@@ -257,6 +257,60 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
   return hip_status(launch_pack_weights(w, n, k, packed, stream));
 }
 
+int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank, const int32_t* permuted_idx,
+                        const void* route_w, int route_w_dtype, const uint16_t* fin_gamma,
+                        float gain_center, float fin_eps, int weight_before_norm, int K,
+                        uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
+                        const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
+                        const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
+                        uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h,
+                        int w_layout, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  // the finalize's checks (P = L) ...
+  if (weight_before_norm < MOETAIL_NORM_GAIN_AFTER || weight_before_norm > MOETAIL_NO_NORM)
+    return MOETAIL_EINVAL;
+  int st = check_norm_args(route_w, route_w_dtype, fin_gamma, fin_eps, K, L, tp, b,
+                           weight_before_norm != MOETAIL_NO_NORM);
+  if (st) return st;
+  if (!a16(rows) || rows_per_rank <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4) ||
+      !a16(latent_partials) || !__builtin_isfinite(gain_center))
+    return MOETAIL_EINVAL;
+  // ... and the tail's
+  if (b < 0 || H <= 0 || I <= 0 || !layout_ok(w_layout)) return MOETAIL_EINVAL;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
+  if (!a16(gamma) || !a16(w_up) || !a16(x) || !a16(w_gate) || !a16(w_upw) || !a16(w_down) ||
+      !a16(out))
+    return MOETAIL_EINVAL;
+  if ((rs && !a16(rs)) || (normed && !a16(normed)) || (h && !a16(h))) return MOETAIL_EINVAL;
+  if (L % 32 || H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
+      b > MOETAIL_MAX_GEMM_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
+  const TailLayout lay = tail_layout(b, L, H, I);
+  if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
+  const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
+  if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+    return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hb = h;
+  if (!hb) {
+    hb = reinterpret_cast<uint16_t*>(ws);
+    ws += lay.h_bytes;
+  }
+  uint16_t* yb = normed;
+  if (!yb) {
+    yb = reinterpret_cast<uint16_t*>(ws);
+    ws += lay.y_bytes;
+  }
+  TailArgs a{x, w_gate, w_upw, w_down, H, I, latent_partials, tp, gamma, eps, w_up, L, b, hb, yb,
+             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout};
+  EpArgs ep{rows, rows_per_rank, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, fin_gamma,
+            gain_center, fin_eps, weight_before_norm, b, K, L, tp, latent_partials, nullptr};
+  hipError_t e = launch_ep_finalize(ep, stream);
+  if (e == hipSuccess) e = launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream);
+  return hip_status(e);
+}
+
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
   if (op == MOETAIL_OP_TP_FINALIZE) {
     if (b <= 0 || b > MOETAIL_MAX_TOKENS || dim0 <= 0 || dim0 > MOETAIL_MAX_ROUTES || dim1 <= 0 ||

@@ -23,59 +23,12 @@
 // instruction reading 1 KB of one row contiguously.
 #include "common.h"
 #include "kernels.h"
+#include "finalize_device.h"
 #include "norm_device.h"
 
 namespace moetail {
 
 namespace {
-
-template <bool WBF16>
-__device__ __forceinline__ float load_weight(const void* w, int64_t i) {
-  if (WBF16) return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(w)[i]) << 16);
-  return reinterpret_cast<const float*>(w)[i];
-}
-
-// Norm modes: kGainAfter (the gain multiplies the normalized row), kGainFirst
-// (weight_before_norm: the gain multiplies before the statistic) and kNoNorm
-// ([tail_runtime] module docstring, the Kimi finalize: the route-weighted
-// row itself, no statistic).
-enum { kGainAfter = 0, kGainFirst = 1, kNoNorm = 2 };
-
-// Route-weighted products of one chunk (normalized unless kNoNorm), added
-// into acc.
-template <int MODE>
-__device__ __forceinline__ void add_products(const uint4& xq, const float (&g)[8], float inv,
-                                             float w, float (&acc)[8]) {
-  float x[8];
-  unpack8(xq, x);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    float n;
-    if (MODE == kGainFirst) {
-      float s = x[c] * g[c];
-      n = s * inv;
-    } else if (MODE == kGainAfter) {
-      float u = x[c] * inv;
-      n = u * g[c];
-    } else {
-      n = x[c];
-    }
-    float p = n * w;
-    acc[c] = acc[c] + p;
-  }
-}
-
-// Lane's share of a chunk's sum of squares (the gains first with kGainFirst).
-template <int MODE>
-__device__ __forceinline__ float chunk_ss(const uint4& xq, const float (&g)[8]) {
-  float v[8];
-  unpack8(xq, v);
-  if (MODE == kGainFirst) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = v[c] * g[c];
-  }
-  return chunk_sum_of_squares(v);
-}
 
 // ------------------------------------------------------- finalize kernel -
 //
@@ -303,77 +256,9 @@ hipError_t finalize_dispatch(const FinArgs& a, int mode, bool w_bf16, hipStream_
 template <int MODE, bool WBF16, int kSlots, int kMaxThreads>
 __global__ void __launch_bounds__(kMaxThreads) rank_finalize_kernel(FinArgs a) {
   __shared__ float block_ss[kSlots][16];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nwaves = (a.P + kBlockCols - 1) / kBlockCols;  // the block: a wave per 512 columns
-  const int t = blockIdx.x;
-  const int d = blockIdx.y;
-  const int P = a.P;
-  const int col = (wave * kWave + lane) * kChunk;
-  const bool has = col < P;
-  const int colc = has ? col : P - kChunk;
-  const uint4 gq = MODE != kNoNorm ? load16(a.gamma + colc) : make_uint4(0, 0, 0, 0);
-  int e = -1;
-  float wk = 0.0f;
-  if (lane < a.K) {
-    e = a.idx[((int64_t)d * a.b + t) * a.K + lane];
-    wk = load_weight<WBF16>(a.w, (int64_t)t * a.K + lane);
-  }
-  uint64_t mask = __ballot(lane < a.K && e >= 0 && (int64_t)e < a.idx_limit);
-  const int np = __popcll(mask);
-
-  float g[8];
-  unpack8(gq, g);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) g[c] = g[c] + a.gain_center;
-  const float inv_width = (float)(1.0 / (double)P);
-  float acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-  const uint16_t* rank_rows = a.rows + (int64_t)d * a.R * P;
-
-  for (int base = 0; base < np; base += kSlots) {
-    const int nb = min(kSlots, np - base);
-    int ks[kSlots];
-    uint4 xq[kSlots];
-    uint64_t m = mask;
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      // Slot s takes the next local route; slots past nb repeat the last.
-      ks[s] = m ? (int)__builtin_ctzll(m) : (s > 0 ? ks[s - 1] : 0);
-      if (m) m &= m - 1;
-      const int row = readlane_i(e, ks[s]);
-      xq[s] = load16(rank_rows + (int64_t)row * P + colc);
-    }
-    mask = m;
-    float my_inv = 0.0f;
-    if (MODE != kNoNorm) {
-      float ss[kSlots];
-#pragma unroll
-      for (int s = 0; s < kSlots; ++s) {
-        ss[s] = has ? chunk_ss<MODE>(xq[s], g) : 0.0f;
-        ss[s] = wave_butterfly_sum(ss[s]);
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int s = 0; s < kSlots; ++s)
-          if (s < nb) block_ss[s][wave] = ss[s];
-      }
-      __syncthreads();
-      if (lane < nb) {
-        float total = 0.0f;
-        for (int j = 0; j < nwaves; ++j) total = total + block_ss[lane][j];
-        my_inv = inv_rms(total, inv_width, a.eps);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      if (s < nb)
-        add_products<MODE>(xq[s], g, readlane_f(my_inv, s), readlane_f(wk, ks[s]), acc);
-    }
-    if (MODE != kNoNorm) __syncthreads();  // block_ss is refilled by the next batch
-  }
-  if (has) store16(a.partials + ((int64_t)d * a.b + t) * P + col, pack8_pz(acc));
+  const RankUnit u{a.rows, a.R, a.idx, a.idx_limit, a.w, a.gamma, a.gain_center, a.eps,
+                   a.b, a.K, a.P, a.partials};
+  rank_partial<MODE, WBF16, kSlots>(u, blockIdx.x, blockIdx.y, block_ss);
 }
 
 // out[t] = bf16(sum over ranks, in rank order from +0, of partials[d][t]),

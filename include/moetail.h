@@ -226,6 +226,37 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The whole decode tail in one call, from the routed experts' GEMM2 rows to
+ * the output row ([tail] module docstring for the finalize; [tail_runtime]
+ * and [shared] for the rest, as in moetail_tail):
+ *     latent_partials = moetail_finalize(rows, ..., partials only)
+ *     out             = moetail_tail(latent_partials, ...)
+ * with the finalize's width P equal to the latent width L.  The results are
+ * the same bits as those two calls in that order (latent_partials is
+ * written, the resident rank-partial buffer): five launches, every argument
+ * of both checked before the first.
+ *
+ *   rows .. K        as in moetail_finalize (fin_gamma, fin_eps: its gamma
+ *                    [L] and eps; weight_before_norm: its norm mode).
+ *   latent_partials  [tp][b][L] BF16 written.
+ *   gamma .. h       as in moetail_tail (gamma [L] and eps: the latent norm's).
+ *   w_layout, workspace: as in moetail_tail (workspace bytes of MOETAIL_OP_TAIL).
+ *   Limits: those of moetail_finalize and moetail_tail.
+ */
+int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank,
+                        const int32_t* permuted_idx, const void* route_w,
+                        int route_w_dtype, const uint16_t* fin_gamma,
+                        float gain_center, float fin_eps, int weight_before_norm,
+                        int K, uint16_t* latent_partials, int tp,
+                        const uint16_t* gamma, float eps, const uint16_t* w_up,
+                        int L, const uint16_t* x, const uint16_t* w_gate,
+                        const uint16_t* w_upw, const uint16_t* w_down, int H,
+                        int I, int b, uint16_t* out, uint16_t* rs,
+                        uint16_t* normed, uint16_t* h, int w_layout,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * The tiled copy of a weight matrix, made once when the weights are loaded
  * (weights are static at decode time).  The projections read either layout
  * (their w_layout argument) and give the same bits from both; the tiled one

@@ -30,8 +30,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
-              "moetail_shared_expert", "moetail_tail", "moetail_pack_weights",
-              "moetail_workspace_bytes", "moetail_status_string"):
+              "moetail_shared_expert", "moetail_tail", "moetail_decode_tail",
+              "moetail_pack_weights", "moetail_workspace_bytes", "moetail_status_string"):
         assert n in names
     assert set(names) == set(mt.ENTRY_POINTS)
 
@@ -231,3 +231,44 @@ def test_workspace_query(b):
     assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168) == b * 16 * 7168 * 2
     assert mt.workspace_bytes(99, b, 1, 1, 1) == 0
     assert mt.workspace_bytes(mt.OP_SHARED_EXPERT, 0, 7168, 6144) == 0
+
+
+def _dt(ws=A, wsb=1 << 31, **kw):
+    a = dict(rows=A, R=128, idx=A, w=A, wdt=mt.F32, fg=A, gc=1.0, feps=1e-6, wbn=1, K=16,
+             lat=A, tp=8, gamma=A, eps=1e-6, wup=A, L=3584, x=A, wg=A, wu=A, wd=A, H=7168,
+             I=6144, b=64, out=A, rs=None, normed=None, h=None, lay=mt.W_TILED)
+    a.update(kw)
+    return mt.lib().moetail_decode_tail(a["rows"], a["R"], a["idx"], a["w"], a["wdt"], a["fg"],
+                                        a["gc"], a["feps"], a["wbn"], a["K"], a["lat"], a["tp"],
+                                        a["gamma"], a["eps"], a["wup"], a["L"], a["x"], a["wg"],
+                                        a["wu"], a["wd"], a["H"], a["I"], a["b"], a["out"],
+                                        a["rs"], a["normed"], a["h"], a["lay"], ws, wsb, None)
+
+
+def test_decode_tail_validation():
+    """Every case is refused before anything launches (the pointers are fake)."""
+    assert _dt(b=0) == mt.OK
+    assert _dt(b=0, rows=None, x=None, ws=None, wsb=0) == mt.OK  # b == 0 before any check
+    # the finalize's checks
+    assert _dt(rows=None) == mt.EINVAL
+    assert _dt(idx=A + 2) == mt.EINVAL
+    assert _dt(w=None) == mt.EINVAL
+    assert _dt(fg=None) == mt.EINVAL
+    assert _dt(fg=None, wbn=mt.NO_NORM, ws=None, wsb=0) == mt.EWORKSPACE  # gamma may be NULL
+    assert _dt(wbn=3) == mt.EINVAL
+    assert _dt(feps=-1.0) == mt.EINVAL
+    assert _dt(gc=float("nan")) == mt.EINVAL
+    assert _dt(lat=None) == mt.EINVAL
+    assert _dt(R=0) == mt.EINVAL
+    assert _dt(K=33) == mt.EUNSUPPORTED
+    assert _dt(tp=33) == mt.EUNSUPPORTED
+    # the tail's checks
+    assert _dt(out=None) == mt.EINVAL
+    assert _dt(wd=A + 2) == mt.EINVAL
+    assert _dt(eps=-1.0) == mt.EINVAL
+    assert _dt(lay=2) == mt.EINVAL
+    assert _dt(L=3600) == mt.EUNSUPPORTED
+    assert _dt(H=7200) == mt.EUNSUPPORTED
+    assert _dt(b=129) == mt.EUNSUPPORTED
+    assert _dt(ws=None, wsb=0) == mt.EWORKSPACE
+    assert _dt(ws=A + 16) == mt.EWORKSPACE

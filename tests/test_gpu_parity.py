@@ -758,3 +758,69 @@ def test_tiled_weights_same_bits_tail(b, tp, L, H, I):
     fused, calls = run_tail_and_calls(up, sh, layout=mt.W_TILED, calls_layout=mt.W_ROWS)
     for key in ("out", "rs", "normed", "h"):
         assert np.array_equal(fused[key], calls[key]), key
+
+
+# ------------------------------------------------- the fused decode tail --
+
+def run_decode_tail(ep, up, sh, mode, wkey="w32", layout=mt.W_TILED):
+    """moetail_decode_tail, and moetail_finalize (partials) then moetail_tail,
+    on the same inputs: (fused outputs, separate outputs)."""
+    tp, b, L = ep["tp"], ep["b"], ep["P"]
+    H, I = sh["H"], sh["I"]
+    rows, idx, w = dev(ep["rows"]), dev(ep["idx"]), dev(ep[wkey])
+    fg = dev(ep["gamma"]) if mode != mt.NO_NORM else None
+    gamma, x = dev(up["gamma"]), dev(sh["x"])
+    w_up, wg, wu, wd = (weight(up["w_up"], layout), weight(sh["w_gate"], layout),
+                        weight(sh["w_up"], layout), weight(sh["w_down"], layout))
+    res = []
+    for fused in (True, False):
+        lat, out = empty_bf16(tp, b, L), empty_bf16(b, H)
+        rs, normed, h = empty_bf16(b, H), empty_bf16(b, L), empty_bf16(b, I)
+        ws = mt.new_workspace(mt.OP_TAIL, b, L, H, I)
+        if fused:
+            mt.moetail_decode_tail(rows, idx, w, fg, ep["gain_center"], ep["eps"], mode, lat, gamma,
+                                   up["eps"], w_up, x, wg, wu, wd, out, rs=rs, normed=normed, h=h,
+                                   workspace=ws, w_layout=layout)
+        else:
+            mt.moetail_finalize(rows, idx, w, fg, ep["gain_center"], ep["eps"], mode, partials=lat)
+            mt.moetail_tail(lat, gamma, up["eps"], w_up, x, wg, wu, wd, out, rs=rs, normed=normed,
+                            h=h, workspace=ws, w_layout=layout)
+        res.append(dict(lat=host(lat), out=host(out), rs=host(rs), normed=host(normed),
+                        h=host(h)))
+    return res
+
+
+@pytest.mark.parametrize("mode,wkey", [(mt.NORM_GAIN_FIRST, "w32"), (mt.NORM_GAIN_AFTER, "w16"),
+                                       (mt.NO_NORM, "w32")])
+def test_decode_tail_decode_scale(mode, wkey):
+    """c2 rows (b=64, K=16, P=3584, tp=8) into c4/c5's tail: the same bits as
+    the two calls, and the partials are the oracle's."""
+    ep = workloads.ep_finalize(90)
+    up = workloads.upproj(91, b=64)
+    sh = workloads.shared(92, b=64)
+    fused, calls = run_decode_tail(ep, up, sh, mode, wkey)
+    for key in ("lat", "out", "rs", "normed", "h"):
+        assert np.array_equal(fused[key], calls[key]), key
+    if mode == mt.NO_NORM:
+        want, _ = oracle.finalize_plain(ep["rows"], ep["idx"], ep[wkey], combine=False,
+                                        nthreads=NT)
+    else:
+        want, _ = oracle.finalize(ep["rows"], ep["idx"], ep[wkey], ep["gamma"], ep["gain_center"],
+                                  ep["eps"], mode == mt.NORM_GAIN_FIRST, combine=False,
+                                  nthreads=NT)
+    assert np.array_equal(fused["lat"], want)
+
+
+@pytest.mark.parametrize("b,K,tp,L,H,I,layout", [(5, 6, 3, 544, 256, 128, mt.W_ROWS),
+                                                 (128, 16, 8, 3584, 512, 192, mt.W_TILED),
+                                                 (3, 4, 2, 8192, 128, 64, mt.W_TILED),
+                                                 (17, 7, 1, 32, 64, 64, mt.W_ROWS)])
+def test_decode_tail_ragged(b, K, tp, L, H, I, layout):
+    """Ragged shapes, b = 128 (8 token blocks), and rows too wide for the side
+    job (P = 8192: the finalize runs as a launch of its own)."""
+    ep = workloads.ep_finalize(b + L, b=b, K=K, P=L, tp=tp)
+    up = workloads.upproj(b + H, b=b, tp=tp, L=L, N=H)
+    sh = workloads.shared(b + I, b=b, H=H, I=I)
+    fused, calls = run_decode_tail(ep, up, sh, mt.NORM_GAIN_FIRST, layout=layout)
+    for key in ("lat", "out", "rs", "normed", "h"):
+        assert np.array_equal(fused[key], calls[key]), key

@@ -55,9 +55,12 @@ ProjTuning tuning(const char* kind) {
                     env_int(kind, "MR"), env_int(kind, "PF")};
 }
 
-// The expert-TP path keeps its rank-summed route rows [b][K][P] BF16.
+// The expert-TP path keeps its rank-summed route rows [b][K][P] BF16, then
+// their sum-of-squares block totals [b][K][ceil(P/512)] FP32.
+size_t tp_rows_bytes(int b, int K, int P) { return round_up(sizeof(uint16_t) * (size_t)b * K * P, 256); }
 size_t tp_workspace(int b, int K, int P) {
-  return round_up(sizeof(uint16_t) * (size_t)b * K * P, 256);
+  return tp_rows_bytes(b, K, P) +
+         round_up(sizeof(float) * (size_t)b * K * ((P + 511) / 512), 256);  // 512-column blocks
 }
 
 struct UpprojLayout {
@@ -154,7 +157,8 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32
     return MOETAIL_EWORKSPACE;
   TpArgs a{kpartials, num_rows, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
            gain_center, eps, weight_before_norm != 0, b, K, P, tp, out,
-           static_cast<uint16_t*>(workspace)};
+           static_cast<uint16_t*>(workspace),
+           reinterpret_cast<float*>(static_cast<char*>(workspace) + tp_rows_bytes(b, K, P))};
   return hip_status(launch_tp_finalize(a, stream));
 }
 

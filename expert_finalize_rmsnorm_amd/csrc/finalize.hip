@@ -332,21 +332,29 @@ hipError_t rank_finalize_dispatch(const FinArgs& a, int mode, bool w_bf16, hipSt
 //
 // x_r = bf16(sum over ranks, in rank order from +0, of the route's
 // K-partials), one wave per (route, 512-column block): pure streaming with
-// every rank's chunk in flight at once.  Absent routes are skipped (the
-// finalize pass never reads them).
+// every rank's chunk in flight at once.  The wave also forms its block's
+// share of the route's sum of squares -- lane l adds the squares of its 8
+// columns of s (x_r, or x_r * g with the gain first) from 0, a wave
+// butterfly gives the block total: the tree's first two levels, so the
+// second pass adds 512-column block totals only.  Absent routes are skipped
+// (the second pass never reads them).
 __global__ void __launch_bounds__(256) tp_rank_sum_kernel(const uint16_t* kpart, int64_t num_rows,
                                                           const int32_t* idx, int routes, int P,
-                                                          int tp, uint16_t* xr) {
+                                                          int tp, uint16_t* xr,
+                                                          const uint16_t* gamma, float gain_center,
+                                                          int gain_first, float* block_total) {
   const int nbk = (P + kBlockCols - 1) / kBlockCols;
   const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // blocks of 4 waves
   if (wid >= (int64_t)routes * nbk) return;
   const int route = (int)(wid / nbk);
   const int j = (int)(wid - (int64_t)route * nbk);
   const int r = idx[route];
-  if (r < 0 || (int64_t)r >= num_rows) return;
-  const int col = (j * kWave + (threadIdx.x & (kWave - 1))) * kChunk;
-  if (col >= P) return;
-  const uint16_t* src = kpart + (int64_t)r * P + col;
+  if (r < 0 || (int64_t)r >= num_rows) return;  // wave-uniform
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = (j * kWave + lane) * kChunk;
+  const bool has = col < P;
+  const int colc = has ? col : P - kChunk;  // lanes past the row read a valid chunk
+  const uint16_t* src = kpart + (int64_t)r * P + colc;
   const int64_t rank_stride = num_rows * (int64_t)P;
   float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   int d = 0;
@@ -368,7 +376,79 @@ __global__ void __launch_bounds__(256) tp_rank_sum_kernel(const uint16_t* kpart,
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
   }
-  store16(xr + (int64_t)route * P + col, pack8(sum));
+  const uint4 q = pack8(sum);
+  if (has) store16(xr + (int64_t)route * P + col, q);
+  float g[8];
+  unpack8(load16(gamma + colc), g);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) g[c] = g[c] + gain_center;
+  float ss = 0.0f;
+  if (has) ss = gain_first ? chunk_ss<kGainFirst>(q, g) : chunk_ss<kGainAfter>(q, g);
+  ss = wave_butterfly_sum(ss);
+  if (lane == 0) block_total[(int64_t)route * nbk + j] = ss;
+}
+
+// The expert-TP finalize's second pass: one thread per 8 columns of a
+// token, blocks of 256 threads over one token's columns.  Every thread first
+// loads its chunk of every route row (the rank-summed rows sit at fixed
+// places in the workspace, absent routes included, so the loads need no
+// index); meanwhile wave 0's lane k forms route k's inverse RMS from the
+// route's block totals (added in column order from 0).  Then the weighted
+// normalized products of the present routes are added in route order from
+// +0.
+template <int MODE, bool WBF16>
+__global__ void __launch_bounds__(256) tp_norm_kernel(const uint16_t* xr, const int32_t* idx,
+                                                      int64_t num_rows, const void* w,
+                                                      const uint16_t* gamma, float gain_center,
+                                                      float eps, int K, int P,
+                                                      const float* block_total, uint16_t* out) {
+  __shared__ float inv_s[MOETAIL_MAX_ROUTES];
+  __shared__ float w_s[MOETAIL_MAX_ROUTES];
+  __shared__ int present_s[MOETAIL_MAX_ROUTES];
+  const int t = blockIdx.y;
+  const int nbk = (P + kBlockCols - 1) / kBlockCols;
+  const int col = (blockIdx.x * 256 + threadIdx.x) * kChunk;
+  const bool has = col < P;
+  const int colc = has ? col : P - kChunk;  // threads past the row read a valid chunk
+  const uint16_t* src = xr + (int64_t)t * K * P + colc;
+  uint4 q[MOETAIL_MAX_ROUTES];
+#pragma unroll
+  for (int k = 0; k < MOETAIL_MAX_ROUTES; ++k)
+    if (k < K) q[k] = load16(src + (int64_t)k * P);
+  const uint4 gq = load16(gamma + colc);
+  if (threadIdx.x < (unsigned)K) {
+    const int k = threadIdx.x;
+    const int r = idx[(int64_t)t * K + k];
+    const bool present = r >= 0 && (int64_t)r < num_rows;
+    float inv = 0.0f;
+    if (present) {
+      // every block total in flight at once (P <= 8192: at most 16), then
+      // added in column order from 0
+      const float* bt = block_total + ((int64_t)t * K + k) * nbk;
+      float v[MOETAIL_MAX_WIDTH / kBlockCols];
+#pragma unroll
+      for (int j = 0; j < MOETAIL_MAX_WIDTH / kBlockCols; ++j) v[j] = j < nbk ? bt[j] : 0.0f;
+      float total = 0.0f;
+#pragma unroll
+      for (int j = 0; j < MOETAIL_MAX_WIDTH / kBlockCols; ++j)
+        if (j < nbk) total = total + v[j];
+      inv = inv_rms(total, (float)(1.0 / (double)P), eps);
+    }
+    inv_s[k] = inv;
+    w_s[k] = load_weight<WBF16>(w, (int64_t)t * K + k);
+    present_s[k] = present;
+  }
+  __syncthreads();
+  if (!has) return;
+  float g[8];
+  unpack8(gq, g);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) g[c] = g[c] + gain_center;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < MOETAIL_MAX_ROUTES; ++k)
+    if (k < K && present_s[k]) add_products<MODE>(q[k], g, inv_s[k], w_s[k], acc);
+  store16(out + (int64_t)t * P + col, pack8_pz(acc));
 }
 
 // ------------------------------------------------------ latent combine ---
@@ -398,17 +478,30 @@ hipError_t launch_ep_finalize(const EpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int MODE, bool WBF16>
+hipError_t tp_norm_launch(const TpArgs& a, hipStream_t s) {
+  const dim3 grid((a.P / kChunk + 255) / 256, a.b);
+  hipLaunchKernelGGL((tp_norm_kernel<MODE, WBF16>), grid, dim3(256), 0, s, a.xr, a.idx,
+                     a.num_rows, a.w, a.gamma, a.gain_center, a.eps, a.K, a.P, a.block_total,
+                     a.out);
+  return hipGetLastError();
+}
+
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
   const int routes = a.b * a.K;
   const int nbk = (a.P + kBlockCols - 1) / kBlockCols;
   const int64_t waves = (int64_t)routes * nbk;
   hipLaunchKernelGGL(tp_rank_sum_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                     a.kpart, a.num_rows, a.idx, routes, a.P, a.tp, a.xr);
+                     a.kpart, a.num_rows, a.idx, routes, a.P, a.tp, a.xr, a.gamma, a.gain_center,
+                     a.wbn != 0 ? 1 : 0, a.block_total);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  FinArgs f{a.xr, 0, a.idx, a.num_rows, 1, a.w, a.gamma, a.gain_center, a.eps,
-            a.b, a.K, a.P, 1, nullptr, a.out, 1};
-  return finalize_dispatch(f, a.wbn != 0 ? kGainFirst : kGainAfter, a.w_bf16 != 0, s);
+  switch ((a.wbn != 0 ? 2 : 0) + (a.w_bf16 != 0 ? 1 : 0)) {
+    case 0: return tp_norm_launch<kGainAfter, false>(a, s);
+    case 1: return tp_norm_launch<kGainAfter, true>(a, s);
+    case 2: return tp_norm_launch<kGainFirst, false>(a, s);
+    default: return tp_norm_launch<kGainFirst, true>(a, s);
+  }
 }
 
 hipError_t launch_latent_norm(const uint16_t* lat, int tp, int b, int L, const uint16_t* gamma,

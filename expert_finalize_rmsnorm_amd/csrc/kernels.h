@@ -40,6 +40,7 @@ struct TpArgs {
   int b, K, P, tp;
   uint16_t* out;          // [b][P]
   uint16_t* xr;           // workspace [b][K][P]: rank-summed route rows
+  float* block_total;     // workspace [b][K][ceil(P/512)]: their sum-of-squares block totals
 };
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t stream);
 

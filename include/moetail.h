@@ -131,7 +131,9 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank,
  *   route_w       [b][K] FP32 or BF16.   gamma [P] BF16.   out [b][P] BF16.
  *   workspace     at least moetail_workspace_bytes(MOETAIL_OP_TP_FINALIZE,
  *                 b, K, P, 0) bytes (the rank-summed route rows x_r,
- *                 [b][K][P] BF16), 256-byte aligned.
+ *                 [b][K][P] BF16, then their sum-of-squares totals per
+ *                 512-column block, [b][K][ceil(P/512)] FP32), 256-byte
+ *                 aligned.
  *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0.
  */
 int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,

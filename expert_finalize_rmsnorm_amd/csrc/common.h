@@ -122,6 +122,17 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// A 16-byte load marked non-temporal: for the large streams read once per
+// call (weights, expert-TP K-partials), so that they pass the caches and
+// what is read again stays in them.  (Marking the split partials', the
+// expert rows' and the latent partials' loads the same way measured
+// neutral.)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ void store16(uint16_t* p, const uint4& q) {
   *reinterpret_cast<uint4*>(p) = q;
 }

@@ -333,12 +333,6 @@ hipError_t rank_finalize_dispatch(const FinArgs& a, int mode, bool w_bf16, hipSt
 // The K-partials are read once: non-temporal loads (streamed past the
 // caches), which keep the rank-summed rows cached for the second pass
 // (measured at b=128, P=7168: 61.3 -> 59.0 us).
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
 // x_r = bf16(sum over ranks, in rank order from +0, of the route's
 // K-partials), one wave per (route, 512-column block): pure streaming with
 // every rank's chunk in flight at once.  The wave also forms its block's

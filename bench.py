@@ -45,12 +45,12 @@ GRAPH_STEPS = 8  # steps per captured graph
 
 
 # HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
-# rocprofv3 --pmc passes over `bench.py --steps 3 --warmup 1 --no-cpu-baseline
+# rocprofv3 --pmc passes over `bench.py --steps 8 --warmup 8 --no-cpu-baseline
 # --no-kernels --copy-calibration`: FETCH_SIZE and WRITE_SIZE per dispatch,
 # scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
 # out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
 # with this digest only.
-TRAFFIC = dict(source_digest="dd039fff91afb8fb", fetch_bytes=180830 * 2 * 1024,
+TRAFFIC = dict(source_digest="4c66771f42537308", fetch_bytes=183472 * 2 * 1024,
                write_bytes=49088 * 1024)
 
 

@@ -49,18 +49,13 @@ namespace {
 //     When the walk passes the last route of a rank, that rank's partial is
 //     rounded to BF16 (-0 as +0), stored if asked, and added in rank order
 //     into the combined row; ranks without local routes give +0 partials.
-//
-// The expert-TP path runs the same kernel in "dense" mode over its rank-
-// summed rows: route k of token t reads row t*K + k of one rank, present
-// when its index lies in [0, idx_limit).
 constexpr int kMaxPairs = MOETAIL_KMAX_PAIRS;
 
 struct FinArgs {
   const uint16_t* rows;
   int64_t R;            // rows per rank (EP)
-  const int32_t* idx;   // EP: [tp][b][K]; dense: [b][K]
+  const int32_t* idx;   // [tp][b][K]
   int64_t idx_limit;    // a route is present when 0 <= idx < idx_limit
-  int dense;
   const void* w;        // [b][K]
   const uint16_t* gamma;
   float gain_center, eps;
@@ -102,7 +97,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
   const int colc = has ? col : P - kChunk;  // lanes past the row read a valid chunk
   const uint4 gq = MODE != kNoNorm ? load16(a.gamma + colc) : make_uint4(0, 0, 0, 0);
   if (wave == 0) {
-    const int nent = a.dense ? a.K : a.tp * a.K;
+    const int nent = a.tp * a.K;
     const int ngroups = (nent + kWave - 1) / kWave;
     const float wk = lane < a.K ? load_weight<WBF16>(a.w, (int64_t)t * a.K + lane) : 0.0f;
     int rr[kMaxPairs / kWave];
@@ -112,7 +107,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
       const int e = kWave * q + lane;
       if (q < ngroups && e < nent) {
         const int d = e / a.K, k = e - d * a.K;
-        rr[q] = a.dense ? a.idx[(int64_t)t * a.K + k] : a.idx[((int64_t)d * a.b + t) * a.K + k];
+        rr[q] = a.idx[((int64_t)d * a.b + t) * a.K + k];
       }
     }
     int base = 0;
@@ -126,7 +121,7 @@ __global__ void __launch_bounds__(kMaxThreads) finalize_kernel(FinArgs a) {
         const uint64_t m = __ballot(local);
         if (local) {
           const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-          const long long row = a.dense ? (long long)t * a.K + k : (long long)d * a.R + rr[q];
+          const long long row = (long long)d * a.R + rr[q];
           pairs[pos] = Pair{row, wsel, d};
         }
         base += __popcll(m);
@@ -470,7 +465,7 @@ __global__ void __launch_bounds__(1024) latent_norm_kernel(const uint16_t* lat, 
 // out is asked for too) a combine pass adds them in rank order; with out
 // only, the fused kernel keeps the partials on chip.
 hipError_t launch_ep_finalize(const EpArgs& a, hipStream_t s) {
-  FinArgs f{a.rows, a.R, a.idx, a.R, 0, a.w, a.gamma, a.gain_center, a.eps,
+  FinArgs f{a.rows, a.R, a.idx, a.R, a.w, a.gamma, a.gain_center, a.eps,
             a.b, a.K, a.P, a.tp, a.partials, a.out, 1};
   if (!a.partials) return finalize_dispatch(f, a.wbn, a.w_bf16 != 0, s);
   hipError_t e = rank_finalize_dispatch(f, a.wbn, a.w_bf16 != 0, s);

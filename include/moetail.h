@@ -203,7 +203,7 @@ int moetail_shared_expert(const uint16_t* x, int b, int H,
  *     out = moetail_combine_norm_upproj(latent_partials, rs) (as that call)
  * with the hidden width H as the up projection's output width N.  The
  * results are the same bits as those two calls in that order; the work is
- * five launches instead of eight: gate/up; {h, y}; {down, up} projections
+ * four launches instead of seven: gate/up; {h, y}; {down, up} projections
  * as one grid; {rs, out}.
  *
  *   latent_partials [tp][b][L], gamma [L], w_up [H][L]: as in

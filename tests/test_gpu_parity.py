@@ -824,3 +824,62 @@ def test_decode_tail_ragged(b, K, tp, L, H, I, layout):
     fused, calls = run_decode_tail(ep, up, sh, mt.NORM_GAIN_FIRST, layout=layout)
     for key in ("lat", "out", "rs", "normed", "h"):
         assert np.array_equal(fused[key], calls[key]), key
+
+
+def test_decode_tail_bench_config_against_oracle():
+    """The benchmark's launch configuration -- moetail_decode_tail at b=64 on
+    tiled weights, c2 rows into c4/c5's tail -- against the oracle: the rank
+    partials and y bit-exact, h, rs and out within the GEMM bar on a sample of
+    tokens (tokens are independent)."""
+    ep = workloads.ep_finalize(0)
+    up = workloads.upproj(0, b=64)
+    sh = workloads.shared(0, b=64)
+    fused, _ = run_decode_tail(ep, up, sh, mt.NORM_GAIN_FIRST)
+    want_lat, _ = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], ep["gain_center"],
+                                  ep["eps"], True, combine=False, nthreads=NT)
+    assert np.array_equal(fused["lat"], want_lat)
+    sel = sample_tokens(64)
+    want_h, want_rs = oracle.shared_expert(sh["x"][sel], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                           nthreads=NT)
+    gemm_bar(fused["h"][sel], want_h, "decode tail h")
+    gemm_bar(fused["rs"][sel], want_rs, "decode tail rs")
+    want_n, want_o = oracle.combine_norm_upproj(want_lat[:, sel], up["gamma"], up["eps"],
+                                                up["w_up"], want_rs, nthreads=NT)
+    assert np.array_equal(fused["normed"][sel], want_n)
+    gemm_bar(fused["out"][sel], want_o, "decode tail out")
+
+
+def test_decode_tail_graph_replay():
+    """Graph replays of the benchmark's call, with eager work and host
+    synchronizations between them: every replay gives the eager bits."""
+    ep = workloads.ep_finalize(7)
+    up = workloads.upproj(7, b=64)
+    sh = workloads.shared(7, b=64)
+    rows, idx, w, fg = dev(ep["rows"]), dev(ep["idx"]), dev(ep["w32"]), dev(ep["gamma"])
+    gamma, x = dev(up["gamma"]), dev(sh["x"])
+    w_up, wg, wu, wd = (mt.pack_weights(dev(a)) for a in (up["w_up"], sh["w_gate"], sh["w_up"],
+                                                          sh["w_down"]))
+    lat, out, rs = empty_bf16(8, 64, 3584), empty_bf16(64, 7168), empty_bf16(64, 7168)
+    ws = mt.new_workspace(mt.OP_TAIL, 64, 3584, 7168, 6144)
+
+    def call():
+        mt.moetail_decode_tail(rows, idx, w, fg, ep["gain_center"], ep["eps"], True, lat, gamma,
+                               up["eps"], w_up, x, wg, wu, wd, out, rs=rs, workspace=ws,
+                               w_layout=mt.W_TILED)
+
+    call()
+    eager = (host(lat), host(out), host(rs))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for _ in range(3):
+        for t in (lat, out, rs):
+            t.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (host(lat), host(out), host(rs))
+        for a, b_ in zip(got, eager):
+            assert np.array_equal(a, b_)

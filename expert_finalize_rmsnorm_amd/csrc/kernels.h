@@ -62,14 +62,16 @@ struct ProjPlan {
   int pf;            // k steps in flight per wave (4 or 8)
   int blocks_per_slice;
   int hold;          // units a wave keeps in registers until its stream ends
+  int passes;        // LDS slices of k_per_split per split (0 or 1: one; more: the multi-pass kernel)
 };
 // Plan knobs: 0 = the library's choice.
 struct ProjTuning {
-  int splits;         // K slices (a power of two)
+  int splits;         // K splits
   int waves;          // waves per block
   int target_blocks;  // blocks in the grid (default: one per CU)
   int mr;             // tiles per wave unit
   int pf;             // prefetch depth
+  int passes;         // LDS slices per split: 0 the plan's choice, 1 one, n >= 2 n
 };
 // Compute units of the current device (queried once; 256 if the query fails).
 int device_cu_count();

@@ -58,6 +58,7 @@ struct FxArgs {
   const uint16_t* rs;  // direct epilogue only: [b][N] or null
   uint16_t* out;       // direct epilogue only: [b][N]
   int tiled;           // weights in the tiled layout (moetail_pack_weights)
+  int passes;          // LDS slices of k_per_split a block's K range spans
 };
 
 // A block barrier for LDS data only: this thread's LDS writes complete,
@@ -118,10 +119,10 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   const int total = my_units * nsteps;
 
   // Weights are read once per call, so their loads are marked non-temporal
-// (streamed past the caches): measured on the b=64 tail step, 102.1 ->
-// 96.3 us, the split partials written at the end of a launch staying
-// cached for the slice sums that read them.
-// Where this lane's 8 weights of a k step lie.  Row-major: row lrow of
+  // (streamed past the caches): measured on the b=64 tail step, 102.1 ->
+  // 96.3 us, the split partials written at the end of a launch staying
+  // cached for the slice sums that read them.
+  // Where this lane's 8 weights of a k step lie.  Row-major: row lrow of
   // the tile, columns 8 kq.. of the step (16 rows x 64 B per wave load).
   // Tiled: the step's 16 x 32 fragment is 1 KB in the accumulator's operand
   // order, lane l at 16 l bytes (one contiguous 1 KB per wave load).  A
@@ -296,6 +297,170 @@ __device__ __forceinline__ void px_body(const FxArgs& a, int block) {
   }
 }
 
+// Multi-pass: a block's K range is `passes` LDS slices of k_per_split.  It
+// stages one slice at a time and streams all of its units over it, each
+// wave holding every one of its units' FP32 accumulators in registers
+// across the passes (kMaxU units at most), so one split partial covers the
+// whole range: fewer partials for the same LDS.  Between passes the block
+// meets at an LDS barrier, restages, and meets again; the weight ring runs
+// on across the boundary (its loads do not depend on the activations).
+// Each unit is still one in-order MFMA chain over its K range.
+template <int NT, int kWaves, int kMaxU>
+__device__ __forceinline__ void px_body_mp(const FxArgs& a, int block) {
+  constexpr int kPF = 8;
+  extern __shared__ uint16_t xs[];  // [16 * NT][pitch]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lrow = lane & 15;
+  const int kq = lane >> 4;
+  const int K = a.K;
+  const int passes = a.passes;
+  const int split = block / a.blocks_per_slice;
+  const int kps = a.k_per_split;
+  const int kb0 = split * kps * passes;  // the plan has K == splits * passes * kps
+  const int nsteps = kps / kKStep;
+  const int stride = a.blocks_per_slice * kWaves;
+  const int u = (block - split * a.blocks_per_slice) * kWaves + wave;
+  const int nunits = a.N / 16;
+  const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // <= kMaxU
+  const int total = my_units * nsteps * passes;
+
+  const int64_t lane_off = a.tiled ? 8 * lane : (int64_t)lrow * K + 8 * kq;
+  const int k_mul = a.tiled ? 16 : 1;
+  const int step_stride = a.tiled ? 512 : kKStep;
+  auto unit_ptr = [&](int i, int pass) {
+    const int row0 = (u + i * stride) * 16;
+    const uint16_t* base = row0 < a.n0 ? a.A0 + (int64_t)row0 * K
+                                       : a.A1 + (int64_t)(row0 - a.n0) * K;
+    return base + lane_off + (int64_t)(kb0 + pass * kps) * k_mul;
+  };
+  // Load cursor over (pass, unit, step), in the order of the MFMAs; past the
+  // wave's last step it stays on it.
+  int l_step = 0, l_i = 0, l_pass = 0, l_left = total;
+  const uint16_t* l_ptr = total > 0 ? unit_ptr(0, 0) : a.A0;
+  auto next_load = [&](uint4& q) {
+    q = load16_stream(l_ptr + l_step * step_stride);
+    if (l_left > 1) {
+      --l_left;
+      if (++l_step == nsteps) {
+        l_step = 0;
+        if (++l_i == my_units) {
+          l_i = 0;
+          ++l_pass;
+        }
+        l_ptr = unit_ptr(l_i, l_pass);
+      }
+    }
+  };
+
+  constexpr int kStage = 16;
+  constexpr int kThreads = kWave * kWaves;
+  const int cpt = kps / 8;  // 16-byte pieces per token and pass
+  const int pieces = 16 * NT * cpt;
+  auto stage_load = [&](int p, int pass) {
+    p = min(p, pieces - 1);
+    const int tok = p / cpt;
+    const int pc = p - tok * cpt;
+    return load16(a.X + (int64_t)min(tok, a.b - 1) * K + kb0 + pass * kps + pc * 8);
+  };
+  auto stage_store = [&](int p, const uint4& q) {
+    if (p < pieces) {
+      const int tok = p / cpt;
+      *reinterpret_cast<uint4*>(xs + tok * a.pitch + (p - tok * cpt) * 8) = q;
+    }
+  };
+  auto stage_rest = [&](int pass, int p_first) {
+    uint4 sq[kStage];
+    for (int p0 = p_first; p0 < pieces; p0 += kStage * kThreads) {
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) sq[j] = stage_load(p0 + j * kThreads, pass);
+#pragma unroll
+      for (int j = 0; j < kStage; ++j) stage_store(p0 + j * kThreads, sq[j]);
+    }
+  };
+
+  // Pass 0's first staging batch goes out before the weight ring (loads
+  // complete in issue order).
+  uint4 sq[kStage];
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) sq[j] = stage_load(threadIdx.x + j * kThreads, 0);
+  uint4 ra[kPF];
+#pragma unroll
+  for (int i = 0; i < kPF; ++i) next_load(ra[i]);
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) stage_store(threadIdx.x + j * kThreads, sq[j]);
+  stage_rest(0, threadIdx.x + kStage * kThreads);
+  lds_barrier();
+
+  // Between passes: every wave done with this pass's activations, the next
+  // pass's staged, every wave sees them.
+  auto restage = [&](int pass) {
+    lds_barrier();
+    stage_rest(pass, threadIdx.x);
+    lds_barrier();
+  };
+  if (total == 0) {
+    for (int p = 1; p < passes; ++p) restage(p);
+    return;
+  }
+
+  f32x4_t acc[NT];
+  f32x4_t hold[kMaxU][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < kMaxU; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) hold[j][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint16_t* xl = xs + lrow * a.pitch + 8 * kq;
+  int c_step = 0, c_i = 0, c_pass = 0;
+
+  for (int q0 = 0; q0 < total; q0 += kPF) {
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) {
+      if (q0 + i < total) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint4 bq =
+              *reinterpret_cast<const uint4*>(xl + 16 * nt * a.pitch + c_step * kKStep);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ra[i]), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0,
+              0, 0);
+        }
+        if (++c_step == nsteps) {
+          // park this unit's sum, take up the next one's (register moves:
+          // the slot index is wave-uniform)
+          c_step = 0;
+          const int next_i = c_i + 1 == my_units ? 0 : c_i + 1;
+#pragma unroll
+          for (int j = 0; j < kMaxU; ++j)
+            if (j == c_i)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) hold[j][nt] = acc[nt];
+#pragma unroll
+          for (int j = 0; j < kMaxU; ++j)
+            if (j == next_i)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) acc[nt] = hold[j][nt];
+          c_i = next_i;
+          if (c_i == 0 && ++c_pass < passes) restage(c_pass);
+        }
+      }
+      next_load(ra[i]);
+    }
+  }
+  // Accumulator lane layout: rows 16 * tile + 4 * (lane / 16) + v, token
+  // 16 * nt + lane % 16; one 1 KB store per (tile, token block).
+  const int ntiles = a.N / 16;
+#pragma unroll
+  for (int j = 0; j < kMaxU; ++j)
+    if (j < my_units)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        a.partials[(((int64_t)split * ntiles + u + j * stride) * NT + nt) * kWave + lane] =
+            hold[j][nt];
+}
+
 // Blocks reach the 8 XCDs in turn (block g on XCD g % 8), and each XCD has
 // its own L2.  The position of block g among the blocks [s, s + m) sorted
 // by (XCD, index): consecutive positions share an XCD, so the blocks of one
@@ -313,12 +478,18 @@ __device__ __forceinline__ int xcd_position(int g, int s, int m) {
 }
 
 __device__ __forceinline__ int fx_blocks(const FxArgs& a) {
-  return a.blocks_per_slice * ((a.K + a.k_per_split - 1) / a.k_per_split);
+  const int range = a.k_per_split * (a.passes > 1 ? a.passes : 1);
+  return a.blocks_per_slice * ((a.K + range - 1) / range);
 }
 
 template <int NT, int MR, int kPF, int kWaves, int kHold>
 __global__ void __launch_bounds__(kWave * kWaves) px_kernel(FxArgs a) {
   px_body<NT, MR, kPF, kWaves, kHold>(a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
+}
+
+template <int NT, int kWaves, int kMaxU>
+__global__ void __launch_bounds__(kWave * kWaves) px_mp_kernel(FxArgs a) {
+  px_body_mp<NT, kWaves, kMaxU>(a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
 }
 
 // Two independent projections in one persistent grid (the fused tail's down
@@ -499,7 +670,73 @@ struct Shape {
 constexpr Shape kShapes[] = {{1, 8, 7},  {1, 8, 8},  {1, 8, 14}, {1, 8, 16}, {2, 4, 4},
                              {2, 4, 7},  {2, 4, 8},  {2, 8, 4},  {2, 8, 7},  {2, 8, 8}};
 
+// The multi-pass plan (two LDS slices per split): units of one tile,
+// prefetch 8, 8 or 12 waves, at most 4 units a wave, every split the same
+// (K a multiple of two slices).  Taken when asked for (tuning runs), or by
+// the default plan when the modelled cost says so.
+ProjPlan make_mp_plan(int b, int rows, int K, const ProjTuning& t) {
+  const int tok = 16 * token_blocks(b);
+  ProjPlan p{};
+  if (tok > 64) return p;
+  const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
+  const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
+  const int tiles = rows / 16;
+  const int passes = t.passes;
+  // the fewest splits (the fewest partials) whose slice fits the LDS and
+  // that give every wave of 8-wave blocks a weight stream; then the waves per
+  // block with the fewest units a wave
+  for (int splits = 1; splits <= 32; ++splits) {
+    if (t.splits > 0 && splits != t.splits) continue;
+    if (K % (passes * splits * kKStep)) continue;
+    const int kps = K / (passes * splits);
+    if (round_up_i(kps, 128) > kmax) continue;
+    const int bps = blocks / splits;
+    if (bps < 1) continue;
+    if (t.splits <= 0 && (int64_t)tiles * splits < (int64_t)blocks * 8) continue;
+    int best_units = 1 << 30;
+    for (int w : {8, 12}) {
+      if (t.waves > 0 && w != t.waves) continue;
+      const int per_wave = (tiles + bps * w - 1) / (bps * w);
+      // units held a wave: 4 at most; with 12 waves (168 registers a wave)
+      // and 4 token blocks, one
+      if (per_wave > 4 || (w == 12 && tok == 64 && per_wave > 1)) continue;
+      if (per_wave < best_units) {
+        best_units = per_wave;
+        p.splits = splits;
+        p.k_per_split = kps;
+        p.pitch = round_up_i(kps, 128) + 8;
+        p.lds = (size_t)tok * p.pitch * sizeof(uint16_t);
+        p.waves = w;
+        p.mr = 1;
+        p.pf = 8;
+        p.blocks_per_slice = bps;
+        p.hold = per_wave;
+        p.passes = passes;
+      }
+    }
+    if (p.splits) return p;
+  }
+  return p;
+}
+
 ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
+  if (t.passes >= 2) {
+    const ProjPlan mp = make_mp_plan(b, rows, K, t);
+    if (mp.splits) return mp;
+  }
+  if (t.passes == 0 && token_blocks(b) == 4) {
+    // The plan's choice: at 4 token blocks the LDS holds at most 1152 of K a
+    // slice, so one pass a split needs 7 or more splits; two passes halve
+    // the split partials.  (At 1 or 2 token blocks the single-pass plan's
+    // extra splits cost less than the multi-pass block's restaging.)
+    ProjTuning t2 = t;
+    t2.passes = 2;
+    const ProjPlan mp = make_mp_plan(b, rows, K, t2);
+    ProjTuning t1 = t;
+    t1.passes = 1;
+    const ProjPlan one = make_plan(b, rows, K, always_partials, t1);
+    return (mp.splits && mp.splits < one.splits) ? mp : one;
+  }
   const int tok = 16 * token_blocks(b);
   const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
   const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
@@ -546,7 +783,7 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   }
   if (best == 1e300 && (t.splits > 0 || t.waves > 0 || t.mr > 0 || t.pf > 0)) {
     // an override that cannot fit: the best plan without it
-    const ProjTuning free_t{0, 0, t.target_blocks, 0, 0};
+    const ProjTuning free_t{0, 0, t.target_blocks, 0, 0, t.passes == 0 ? 0 : 1};
     return make_plan(b, rows, K, always_partials, free_t);
   }
   return p;  // splits == 0: no slice of K fits the LDS
@@ -586,7 +823,58 @@ hipError_t px_dispatch_hold(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   }
 }
 
+template <int NT, int W, int U>
+hipError_t mp_launch(const FxArgs& a0, const ProjPlan& p, hipStream_t s) {
+  static bool attr_set = false;  // idempotent: every call sets the same maximum
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_mp_kernel<NT, W, U>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  FxArgs a = a0;
+  a.passes = p.passes;
+  hipLaunchKernelGGL((px_mp_kernel<NT, W, U>), dim3(p.splits * p.blocks_per_slice),
+                     dim3(kWave * W), p.lds, s, a);
+  return hipGetLastError();
+}
+
+template <int W, int U>
+hipError_t mp_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  switch (token_blocks(a.b)) {
+    case 1: return mp_launch<1, W, U>(a, p, s);
+    case 2: return mp_launch<2, W, U>(a, p, s);
+    case 4: return mp_launch<4, W, U>(a, p, s);
+    default: return hipErrorInvalidValue;  // not planned (more than 4 token blocks)
+  }
+}
+
+// 12 waves holding 2 or 4 units: up to 2 token blocks (4 spill registers).
+template <int U>
+hipError_t mp_dispatch12_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  switch (token_blocks(a.b)) {
+    case 1: return mp_launch<1, 12, U>(a, p, s);
+    case 2: return mp_launch<2, 12, U>(a, p, s);
+    default: return hipErrorInvalidValue;  // not planned
+  }
+}
+
+hipError_t mp_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (!a.partials) return hipErrorInvalidValue;  // the multi-pass kernel always writes partials
+  const int u = p.hold <= 1 ? 1 : p.hold <= 2 ? 2 : 4;
+  if (p.waves == 12 && token_blocks(a.b) == 4 && u > 1) return hipErrorInvalidValue;  // not planned
+  switch ((p.waves == 12 ? 3 : 0) + (u == 1 ? 0 : u == 2 ? 1 : 2)) {
+    case 0: return mp_dispatch_nt<8, 1>(a, p, s);
+    case 1: return mp_dispatch_nt<8, 2>(a, p, s);
+    case 2: return mp_dispatch_nt<8, 4>(a, p, s);
+    case 3: return mp_dispatch_nt<12, 1>(a, p, s);
+    case 4: return mp_dispatch12_nt<2>(a, p, s);
+    default: return mp_dispatch12_nt<4>(a, p, s);
+  }
+}
+
 hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (p.passes > 1) return mp_dispatch(a, p, s);
   if (p.hold && a.partials) {
     if (p.mr != 1 || p.pf != 8 || p.waves > 8 || token_blocks(a.b) > 4) return hipErrorInvalidValue;
     return p.waves == 7 ? px_dispatch_hold<7>(a, p, s) : px_dispatch_hold<8>(a, p, s);
@@ -657,13 +945,15 @@ ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const Pro
 
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
   const size_t tok = 16 * (size_t)token_blocks(b);  // padded tokens are stored too
-  return (p.splits > 1 || always) ? sizeof(float) * (size_t)p.splits * tok * n_out : 0;
+  return (p.splits > 1 || p.passes > 1 || always) ? sizeof(float) * (size_t)p.splits * tok * n_out
+                                                   : 0;
 }
 
 // The CUs split between the two projections (each keeping its K slices),
 // waves per block 7 or 8: the split that minimizes the longest wave stream
 // (units per wave times k steps per unit), then the fewest idle blocks.
 GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
+  if (p0.passes > 1 || p1.passes > 1) return GroupPlan{0, 0, 0, 0};  // one slice per split only
   const int cu = device_cu_count();
   const int tok = 16 * token_blocks(b);
   GroupPlan best{0, 0, 0, 0};
@@ -746,7 +1036,7 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* pa
 hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint16_t* X, int b,
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
-  const bool split = plan.splits > 1;
+  const bool split = plan.splits > 1 || plan.passes > 1;
   f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
            split ? part : nullptr, rs, out, tiled};

@@ -401,14 +401,20 @@ def test_shared_unit_rows():
 PLAN_OVERRIDES = [dict(WAVES=w, SPLITS=s) for w in (7, 8, 14, 16) for s in (2, 8)] + [
     dict(MR=2, PF=f, WAVES=w, SPLITS=s) for f in (4, 8) for w in (4, 7, 8) for s in (2, 8)] + [
     dict(WAVES=8, SPLITS=2, BLOCKS=100), dict(WAVES=14, SPLITS=8, BLOCKS=37),
-    dict(MR=2, PF=4, WAVES=7, SPLITS=8, BLOCKS=37), dict(SPLITS=1)]
+    dict(MR=2, PF=4, WAVES=7, SPLITS=8, BLOCKS=37), dict(SPLITS=1)] + [
+    # the multi-pass kernel: 2 or 4 LDS slices per split, 8 or 12 waves, 1..4
+    # held units; and the single-pass kernel where the plan would pick it
+    dict(PASSES=1), dict(PASSES=2), dict(PASSES=2, BLOCKS=64), dict(PASSES=4, BLOCKS=64),
+    dict(PASSES=2, SPLITS=1), dict(PASSES=2, WAVES=8, BLOCKS=64), dict(PASSES=2, BLOCKS=16),
+    dict(PASSES=2, BLOCKS=4), dict(PASSES=2, WAVES=12, BLOCKS=8)]
 
 
 @pytest.mark.parametrize("b", [1, 40, 128])
 def test_projection_plan_overrides(b, monkeypatch):
     """Every kernel shape the plan can pick (waves per block, slice count,
-    uneven blocks per slice) against the oracle, through the tuning
-    overrides; a slice count that does not fit falls back to the default."""
+    uneven blocks per slice, LDS passes per slice) against the oracle,
+    through the tuning overrides; a slice count that does not fit falls back
+    to the default."""
     up = workloads.upproj(70 + b, b=b, tp=2, L=3584, N=512, with_rs=True)
     sh = workloads.shared(80 + b, b=b, H=1024, I=1024)
     want_up = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"], up["rs"],
@@ -417,7 +423,7 @@ def test_projection_plan_overrides(b, monkeypatch):
                                            nthreads=NT)
     for ov in PLAN_OVERRIDES:
         for kind in ("UPPROJ", "GATEUP", "DOWN"):
-            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF"):
+            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF", "PASSES"):
                 if key in ov:
                     monkeypatch.setenv(f"MOETAIL_{kind}_{key}", str(ov[key]))
                 else:

@@ -50,8 +50,8 @@ GRAPH_STEPS = 8  # steps per captured graph
 # scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
 # out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
 # with this digest only.
-TRAFFIC = dict(source_digest="5950403dd99ba974", fetch_bytes=177437 * 2 * 1024,
-               write_bytes=36800 * 1024)
+TRAFFIC = dict(source_digest="1501562b16dbe671", fetch_bytes=176014 * 2 * 1024,
+               write_bytes=33216 * 1024)
 
 
 def kernel_source_digest():

@@ -9,7 +9,6 @@
 
 #include <stdio.h>
 #include <stdlib.h>
-#include <string.h>
 
 #include "kernels.h"
 
@@ -45,19 +44,17 @@ bool layout_ok(int w_layout) {
 // environment at every call (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES,
 // _BLOCKS, _MR, _PF and _PASSES for KIND in UPPROJ, GATEUP, DOWN.  An override
 // that names no built kernel shape, or a slice that does not fit, is ignored.
-// Passes: 0 lets the plan choose (the gate/up default), 1 is one LDS slice
-// per split (the down and up projections' default: the fused tail runs them
-// as one single-pass grid), 2 or more that many slices per split.
-int env_int(const char* kind, const char* knob, int fallback = 0) {
+// Passes: 0 (the default) lets the plan choose, 1 is one LDS slice per
+// split, 2 or more that many slices per split.
+int env_int(const char* kind, const char* knob) {
   char name[64];
   snprintf(name, sizeof name, "MOETAIL_%s_%s", kind, knob);
   const char* v = getenv(name);
-  return v ? atoi(v) : fallback;
+  return v ? atoi(v) : 0;
 }
 ProjTuning tuning(const char* kind) {
-  const int passes = env_int(kind, "PASSES", strcmp(kind, "GATEUP") == 0 ? 0 : 1);
   return ProjTuning{env_int(kind, "SPLITS"), env_int(kind, "WAVES"), env_int(kind, "BLOCKS"),
-                    env_int(kind, "MR"), env_int(kind, "PF"), passes};
+                    env_int(kind, "MR"), env_int(kind, "PF"), env_int(kind, "PASSES")};
 }
 
 // The expert-TP path keeps its rank-summed route rows [b][K][P] BF16, then

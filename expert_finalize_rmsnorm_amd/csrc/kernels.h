@@ -88,6 +88,7 @@ struct GroupPlan {
   int bps0, bps1;
   int waves;
   int hold;
+  int mp;  // both in the multi-pass kernel (either plan has passes > 1)
 };
 GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1);
 

@@ -26,6 +26,10 @@
 //    block per CU; their FP32 partials are added in slice order by a small
 //    second kernel, which also applies the epilogue (rs add, or SiLU for
 //    gate/up) and the single BF16 rounding, -0 written as +0.
+//  * At 4 token blocks a slice holds at most 1152 of K, so a block may run
+//    its K range as two LDS passes with every unit's sum kept in registers
+//    across them (px_mp_kernel): half the split partials.  The b=64 gate/up
+//    and down projections run that way.
 // Results are deterministic: the slice sum order is fixed and each slice is
 // one wave's in-order MFMA chain, whichever block runs it.
 #include "common.h"
@@ -317,8 +321,11 @@ __device__ __forceinline__ void px_body_mp(const FxArgs& a, int block) {
   const int passes = a.passes;
   const int split = block / a.blocks_per_slice;
   const int kps = a.k_per_split;
-  const int kb0 = split * kps * passes;  // the plan has K == splits * passes * kps
-  const int nsteps = kps / kKStep;
+  const int kb0 = split * kps * passes;
+  // A multi-pass plan has K == splits * passes * kps; a single-pass plan
+  // run here (one pass) may end in a shorter slice.
+  const int klen = passes > 1 ? kps : min(kps, K - kb0);
+  const int nsteps = klen / kKStep;
   const int stride = a.blocks_per_slice * kWaves;
   const int u = (block - split * a.blocks_per_slice) * kWaves + wave;
   const int nunits = a.N / 16;
@@ -355,7 +362,7 @@ __device__ __forceinline__ void px_body_mp(const FxArgs& a, int block) {
 
   constexpr int kStage = 16;
   constexpr int kThreads = kWave * kWaves;
-  const int cpt = kps / 8;  // 16-byte pieces per token and pass
+  const int cpt = klen / 8;  // 16-byte pieces per token and pass
   const int pieces = 16 * NT * cpt;
   auto stage_load = [&](int p, int pass) {
     p = min(p, pieces - 1);
@@ -501,6 +508,18 @@ __global__ void __launch_bounds__(kWave * kWaves) px_group_kernel(FxArgs a0, FxA
     px_body<NT, 1, 8, kWaves, kHold>(a0, xcd_position(blockIdx.x, 0, blocks0));
   else
     px_body<NT, 1, 8, kWaves, kHold>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
+}
+
+// The same two projections, both in the multi-pass form: a single-pass plan
+// runs as one pass (the same k-step order into one accumulator, the same
+// partial layout, so the same sums as its own launch).
+template <int NT, int kWaves, int kMaxU>
+__global__ void __launch_bounds__(kWave * kWaves) px_group_mp_kernel(FxArgs a0, FxArgs a1,
+                                                                     int blocks0) {
+  if ((int)blockIdx.x < blocks0)
+    px_body_mp<NT, kWaves, kMaxU>(a0, xcd_position(blockIdx.x, 0, blocks0));
+  else
+    px_body_mp<NT, kWaves, kMaxU>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
 }
 
 // Slice partials added in slice order, then the epilogue: one thread per
@@ -726,9 +745,11 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   }
   if (t.passes == 0 && token_blocks(b) == 4) {
     // The plan's choice: at 4 token blocks the LDS holds at most 1152 of K a
-    // slice, so one pass a split needs 7 or more splits; two passes halve
-    // the split partials.  (At 1 or 2 token blocks the single-pass plan's
-    // extra splits cost less than the multi-pass block's restaging.)
+    // slice, so one pass a split needs 7 or more splits; two passes cut the
+    // split partials (b=64: gate/up 8 -> 4 splits, down 8 -> 6; the up
+    // projection keeps its 4).  At 1 or 2 token blocks the single-pass
+    // plan's extra splits cost less than the multi-pass block's restaging
+    // (measured: the shared expert at b=16 lost 2 us).
     ProjTuning t2 = t;
     t2.passes = 2;
     const ProjPlan mp = make_mp_plan(b, rows, K, t2);
@@ -910,6 +931,46 @@ hipError_t group_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blo
   return hipGetLastError();
 }
 
+template <int NT, int W, int U>
+hipError_t group_mp_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
+                           size_t lds, hipStream_t s) {
+  static bool attr_set = false;  // idempotent: every call sets the same maximum
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_group_mp_kernel<NT, W, U>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((px_group_mp_kernel<NT, W, U>), dim3(blocks), dim3(kWave * W), lds, s, a0,
+                     a1, blocks0);
+  return hipGetLastError();
+}
+
+// 8 waves hold up to 4 units; 12 waves (168 registers a wave) up to 4 with
+// 1 or 2 token blocks, one with 4.
+hipError_t group_mp_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g, int blocks0,
+                             int blocks, size_t lds, hipStream_t s) {
+  const int ntb = token_blocks(a0.b);
+  if (g.hold > 4 || (g.waves == 12 && ntb == 4 && g.hold > 1)) return hipErrorInvalidValue;
+  if (g.waves == 8) {
+    switch (ntb) {
+      case 1: return group_mp_launch<1, 8, 4>(a0, a1, blocks0, blocks, lds, s);
+      case 2: return group_mp_launch<2, 8, 4>(a0, a1, blocks0, blocks, lds, s);
+      case 4: return group_mp_launch<4, 8, 4>(a0, a1, blocks0, blocks, lds, s);
+      default: return hipErrorInvalidValue;  // not planned
+    }
+  }
+  if (g.waves == 12) {
+    switch (ntb) {
+      case 1: return group_mp_launch<1, 12, 4>(a0, a1, blocks0, blocks, lds, s);
+      case 2: return group_mp_launch<2, 12, 4>(a0, a1, blocks0, blocks, lds, s);
+      case 4: return group_mp_launch<4, 12, 1>(a0, a1, blocks0, blocks, lds, s);
+      default: return hipErrorInvalidValue;  // not planned
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int W, int H>
 hipError_t group_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
                              size_t lds, hipStream_t s) {
@@ -952,11 +1013,44 @@ size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
 // The CUs split between the two projections (each keeping its K slices),
 // waves per block 7 or 8: the split that minimizes the longest wave stream
 // (units per wave times k steps per unit), then the fewest idle blocks.
-GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
-  if (p0.passes > 1 || p1.passes > 1) return GroupPlan{0, 0, 0, 0};  // one slice per split only
+// With a multi-pass plan on either side, both run in the multi-pass kernel:
+// 8 or 12 waves, the split with the shortest longest wave stream (units per
+// wave times k steps per unit, all passes), then the most blocks.
+GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
   const int cu = device_cu_count();
   const int tok = 16 * token_blocks(b);
-  GroupPlan best{0, 0, 0, 0};
+  GroupPlan best{0, 0, 0, 0, 0};
+  if (tok > 64) return best;
+  const long long n0 = (long long)(p0.passes > 1 ? p0.passes : 1) * (p0.k_per_split / kKStep);
+  const long long n1 = (long long)(p1.passes > 1 ? p1.passes : 1) * (p1.k_per_split / kKStep);
+  long long best_cost = -1;
+  int best_blocks = 0;
+  for (int w : {8, 12}) {
+    for (int bps0 = 1; bps0 * p0.splits < cu; ++bps0) {
+      const int bps1 = (cu - bps0 * p0.splits) / p1.splits;
+      if (bps1 < 1) break;
+      const int pw0 = ((rows0 / 16) + bps0 * w - 1) / (bps0 * w);
+      const int pw1 = ((rows1 / 16) + bps1 * w - 1) / (bps1 * w);
+      const int pw = pw0 > pw1 ? pw0 : pw1;
+      if (pw > 4 || (w == 12 && tok == 64 && pw > 1)) continue;  // registers: as the plan's
+      const long long c0 = pw0 * n0, c1 = pw1 * n1;
+      const long long cost = c0 > c1 ? c0 : c1;
+      const int blocks = bps0 * p0.splits + bps1 * p1.splits;
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && blocks > best_blocks)) {
+        best_cost = cost;
+        best_blocks = blocks;
+        best = GroupPlan{bps0, bps1, w, pw, 1};
+      }
+    }
+  }
+  return best;
+}
+
+GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
+  if (p0.passes > 1 || p1.passes > 1) return plan_group_mp(b, p0, rows0, p1, rows1);
+  const int cu = device_cu_count();
+  const int tok = 16 * token_blocks(b);
+  GroupPlan best{0, 0, 0, 0, 0};
   long long best_cost = -1;
   int best_blocks = 0;
   for (int w = 7; w <= 8; ++w) {
@@ -972,7 +1066,7 @@ GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, i
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && blocks > best_blocks)) {
         best_cost = cost;
         best_blocks = blocks;
-        best = GroupPlan{bps0, bps1, w, (tok <= 64 && pw0 <= 4 && pw1 <= 4) ? 4 : 0};
+        best = GroupPlan{bps0, bps1, w, (tok <= 64 && pw0 <= 4 && pw1 <= 4) ? 4 : 0, 0};
       }
     }
   }
@@ -1009,7 +1103,11 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   const int blocks0 = g.bps0 * down.splits;
   const int blocks = blocks0 + g.bps1 * up.splits;
   const size_t lds = down.lds > up.lds ? down.lds : up.lds;
-  if (g.waves == 7)
+  if (g.mp) {
+    dn.passes = down.passes > 1 ? down.passes : 1;
+    upa.passes = up.passes > 1 ? up.passes : 1;
+    e = group_mp_dispatch(dn, upa, g, blocks0, blocks, lds, s);
+  } else if (g.waves == 7)
     e = g.hold ? group_dispatch_nt<7, 4>(dn, upa, blocks0, blocks, lds, s)
                : group_dispatch_nt<7, 0>(dn, upa, blocks0, blocks, lds, s);
   else if (g.waves == 8)

@@ -611,6 +611,43 @@ def test_tail_ragged(b, tp, L, H, I):
     gemm_bar(fused["out"], want_o, "tail out")
 
 
+TAIL_OVERRIDES = [
+    dict(DOWN_PASSES=2, DOWN_BLOCKS=16),                      # down multi-pass, up single-pass
+    dict(UPPROJ_PASSES=2, UPPROJ_BLOCKS=16, DOWN_SPLITS=3),   # down single-pass, ragged last slice
+    dict(DOWN_PASSES=2, DOWN_BLOCKS=16, UPPROJ_SPLITS=3),     # up single-pass, ragged last slice
+    dict(DOWN_PASSES=4, DOWN_BLOCKS=8, UPPROJ_PASSES=2, UPPROJ_BLOCKS=8),
+    dict(GATEUP_PASSES=2, GATEUP_BLOCKS=16, DOWN_PASSES=1, UPPROJ_PASSES=1),
+]
+
+
+@pytest.mark.parametrize("b", [8, 40])
+def test_tail_plan_overrides(b, monkeypatch):
+    """The fused tail's grouped launch in its multi-pass form (either side
+    multi-pass, the other run as one pass, with a shorter last slice) gives
+    the bits of the two calls, and both match the oracle."""
+    tp, L, H, I = 2, 1024, 512, 320
+    up = workloads.upproj(90 + b, b=b, tp=tp, L=L, N=H)
+    sh = workloads.shared(95 + b, b=b, H=H, I=I)
+    want_h, want_rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                           nthreads=NT)
+    want_o = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"], want_rs,
+                                        nthreads=NT)[1]
+    for ov in TAIL_OVERRIDES:
+        for kind in ("UPPROJ", "GATEUP", "DOWN"):
+            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF", "PASSES"):
+                name = f"{kind}_{key}"
+                if name in ov:
+                    monkeypatch.setenv(f"MOETAIL_{name}", str(ov[name]))
+                else:
+                    monkeypatch.delenv(f"MOETAIL_{name}", raising=False)
+        fused, calls = run_tail_and_calls(up, sh, layout=mt.W_TILED)
+        for k in ("out", "rs", "normed", "h"):
+            assert np.array_equal(fused[k], calls[k]), f"{k} {ov}"
+        gemm_bar(fused["h"], want_h, f"tail h b={b} {ov}")
+        gemm_bar(fused["rs"], want_rs, f"tail rs b={b} {ov}")
+        gemm_bar(fused["out"], want_o, f"tail out b={b} {ov}")
+
+
 def test_tail_graph_replay():
     up = workloads.upproj(5, b=64)
     sh = workloads.shared(5, b=64)

@@ -416,24 +416,26 @@ __global__ void __launch_bounds__(256) tp_norm_kernel(const uint16_t* xr, const 
   const uint4 gq = load16(gamma + colc);
   if (threadIdx.x < (unsigned)K) {
     const int k = threadIdx.x;
+    // The route's index, its block totals (P <= 8192: at most 16) and its
+    // weight are loaded at once: the totals sit at a fixed place whether or
+    // not the route is present (an absent route's are never used).
     const int r = idx[(int64_t)t * K + k];
+    const float* bt = block_total + ((int64_t)t * K + k) * nbk;
+    float v[MOETAIL_MAX_WIDTH / kBlockCols];
+#pragma unroll
+    for (int j = 0; j < MOETAIL_MAX_WIDTH / kBlockCols; ++j) v[j] = j < nbk ? bt[j] : 0.0f;
+    const float wk = load_weight<WBF16>(w, (int64_t)t * K + k);
     const bool present = r >= 0 && (int64_t)r < num_rows;
     float inv = 0.0f;
     if (present) {
-      // every block total in flight at once (P <= 8192: at most 16), then
-      // added in column order from 0
-      const float* bt = block_total + ((int64_t)t * K + k) * nbk;
-      float v[MOETAIL_MAX_WIDTH / kBlockCols];
-#pragma unroll
-      for (int j = 0; j < MOETAIL_MAX_WIDTH / kBlockCols; ++j) v[j] = j < nbk ? bt[j] : 0.0f;
-      float total = 0.0f;
+      float total = 0.0f;  // in column order from 0
 #pragma unroll
       for (int j = 0; j < MOETAIL_MAX_WIDTH / kBlockCols; ++j)
         if (j < nbk) total = total + v[j];
       inv = inv_rms(total, (float)(1.0 / (double)P), eps);
     }
     inv_s[k] = inv;
-    w_s[k] = load_weight<WBF16>(w, (int64_t)t * K + k);
+    w_s[k] = wk;
     present_s[k] = present;
   }
   __syncthreads();

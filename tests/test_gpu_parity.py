@@ -617,6 +617,8 @@ TAIL_OVERRIDES = [
     dict(DOWN_PASSES=2, DOWN_BLOCKS=16, UPPROJ_SPLITS=3),     # up single-pass, ragged last slice
     dict(DOWN_PASSES=4, DOWN_BLOCKS=8, UPPROJ_PASSES=2, UPPROJ_BLOCKS=8),
     dict(GATEUP_PASSES=2, GATEUP_BLOCKS=16, DOWN_PASSES=1, UPPROJ_PASSES=1),
+    # the single-pass side planned with 2-tile units (run one tile a unit)
+    dict(DOWN_PASSES=2, DOWN_BLOCKS=16, UPPROJ_MR=2, UPPROJ_PF=4, UPPROJ_WAVES=7, UPPROJ_SPLITS=2),
 ]
 
 

@@ -102,7 +102,7 @@ def main():
                          "1: the three calls in order on one stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the tp rank partials are a resident buffer on one device).", file=sys.stderr)
         sys.exit(2)
 

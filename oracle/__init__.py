@@ -23,6 +23,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 W_F32 = 0
 W_BF16 = 1
+SS_W64 = 0  # the wave64 sum-of-squares tree (default)
+SS_SEQ = 1  # plain sequential sum of squares
 
 # -O2 with contraction off and no fast-math: every FP32 operation rounds on
 # its own, exactly as the C source is written.
@@ -51,6 +53,12 @@ def lib():
         _lib.oracle_bf16_round.argtypes = [P, P, I64]
         _lib.oracle_sum_of_squares.argtypes = [P, I32]
         _lib.oracle_sum_of_squares.restype = F32
+        _lib.oracle_set_ss_order.argtypes = [I32]
+        _lib.oracle_set_ss_order.restype = None
+        _lib.oracle_inv_rms.argtypes = [F32, I32, F32]
+        _lib.oracle_inv_rms.restype = F32
+        _lib.oracle_route_products.argtypes = [P, P, F32, F32, F32, I32, I32, P]
+        _lib.oracle_route_products.restype = None
         _lib.oracle_finalize.argtypes = [P, I64, P, P, I32, P, F32, F32, I32,
                                          I32, I32, I32, I32, P, P, I32]
         _lib.oracle_finalize_plain.argtypes = [P, I64, P, P, I32, I32, I32, I32, I32, P, P,
@@ -106,6 +114,39 @@ def f32(h) -> np.ndarray:
 def sum_of_squares(v) -> np.float32:
     v = np.ascontiguousarray(v, dtype=np.float32)
     return np.float32(lib().oracle_sum_of_squares(_ptr(v), v.shape[-1]))
+
+
+class ss_order:
+    """Context manager: the oracle's sum-of-squares order (SS_W64 or SS_SEQ)
+    inside the block, the wave64 tree again after it."""
+
+    def __init__(self, order):
+        self.order = order
+
+    def __enter__(self):
+        lib().oracle_set_ss_order(self.order)
+        return self
+
+    def __exit__(self, *exc):
+        lib().oracle_set_ss_order(SS_W64)
+        return False
+
+
+def inv_rms(ss, P, eps) -> np.float32:
+    """1 / sqrt(ss * fp32(1/P) + eps), correctly rounded to FP32."""
+    return np.float32(lib().oracle_inv_rms(float(np.float32(ss)), int(P), float(np.float32(eps))))
+
+
+def route_products(x, gamma, gain_center, w, eps, weight_before_norm) -> np.ndarray:
+    """One BF16 row x [P] -> its weighted, normalized FP32 products [P]."""
+    x = _u16(x)
+    gamma = _u16(gamma)
+    P = x.shape[-1]
+    p = np.empty(P, np.float32)
+    lib().oracle_route_products(_ptr(x), _ptr(gamma), float(np.float32(gain_center)),
+                                float(np.float32(w)), float(np.float32(eps)),
+                                int(bool(weight_before_norm)), P, _ptr(p))
+    return p
 
 
 def finalize(rows, idx, w, gamma, gain_center, eps, weight_before_norm,

@@ -68,6 +68,16 @@ static float route_weight(const void* w, int w_dtype, int64_t i) {
 
 /* ------------------------------------------------------ sum of squares -- */
 
+/* The sum-of-squares order, chosen by oracle_set_ss_order (W64 unless set):
+ * the tree below, or the plain sequential sum (SEQ), which shows that the
+ * acceptance bar (within 1 BF16 step, at least 99.9% bit-exact) does not
+ * depend on the tree.  Tests set it between calls, never during one. */
+static int ss_order = ORACLE_SS_W64;
+
+void oracle_set_ss_order(int order) {
+    ss_order = order == ORACLE_SS_SEQ ? ORACLE_SS_SEQ : ORACLE_SS_W64;
+}
+
 /* The sum-of-squares tree.  [tail] _TpTailKernel.warp_sum_of_squares: each
  * thread owns 8 consecutive columns and adds their squares one by one from
  * 0.0; an xor butterfly over the warp's lanes makes the warp total; warps
@@ -78,7 +88,7 @@ static float route_weight(const void* w, int w_dtype, int64_t i) {
  * lane holds the block total; the block totals are added in ascending
  * block order from 0.0 (one band: the band split of the pages is a
  * property of an NVIDIA SM count).  Columns at or past P add nothing. */
-float oracle_sum_of_squares(const float* v, int P) {
+static float sum_of_squares_w64(const float* v, int P) {
     float total = 0.0f;
     for (int block = 0; block * 512 < P; ++block) {
         float lane[64], next[64];
@@ -102,6 +112,20 @@ float oracle_sum_of_squares(const float* v, int P) {
     return total;
 }
 
+/* The plain order: squares added one by one in column order from 0.0. */
+static float sum_of_squares_seq(const float* v, int P) {
+    float total = 0.0f;
+    for (int c = 0; c < P; ++c) {
+        float sq = v[c] * v[c];
+        total = total + sq;
+    }
+    return total;
+}
+
+float oracle_sum_of_squares(const float* v, int P) {
+    return ss_order == ORACLE_SS_SEQ ? sum_of_squares_seq(v, P) : sum_of_squares_w64(v, P);
+}
+
 /* 1 / sqrt(mean + eps).  [tail] _TpTailKernel: total * (1.0 / POOLED) + eps
  * then rsqrt.  Readings: 1/P is the FP32 nearest to the double 1.0/P; the
  * multiply and the add are two FP32 roundings; rsqrt is taken correctly
@@ -112,6 +136,8 @@ static float inv_rms(float ss, int P, float eps) {
     m = m + eps;
     return (float)(1.0 / sqrt((double)m));
 }
+
+float oracle_inv_rms(float ss, int P, float eps) { return inv_rms(ss, P, eps); }
 
 /* One route row x[P] (BF16) -> its weighted, normalized FP32 products p[P].
  * [tail] module docstring: s_r = x_r * (gamma + gain_center) with
@@ -146,6 +172,16 @@ static void route_products(const uint16_t* x, const float* gain, float w,
 static void make_gains(const uint16_t* gamma, float gain_center, int P,
                        float* gain) {
     for (int c = 0; c < P; ++c) gain[c] = f32_of(gamma[c]) + gain_center;
+}
+
+void oracle_route_products(const uint16_t* x, const uint16_t* gamma, float gain_center,
+                           float w, float eps, int weight_before_norm, int P, float* p) {
+    float* gain = (float*)malloc(sizeof(float) * (size_t)P);
+    float* v = (float*)malloc(sizeof(float) * (size_t)P);
+    make_gains(gamma, gain_center, P, gain);
+    route_products(x, gain, w, eps, weight_before_norm, P, v, p);
+    free(gain);
+    free(v);
 }
 
 /* ------------------------------------------------------- EP finalize ---- */

@@ -31,11 +31,25 @@ extern "C" {
 #define ORACLE_W_F32 0
 #define ORACLE_W_BF16 1
 
+/* Sum-of-squares orders (oracle_set_ss_order). */
+#define ORACLE_SS_W64 0 /* the wave64 tree (default) */
+#define ORACLE_SS_SEQ 1 /* plain sequential sum in column order */
+
 /* IEEE round-to-nearest-even of n floats to BF16 bit patterns. */
 void oracle_bf16_round(const float* x, uint16_t* y, int64_t n);
 
-/* The fixed sum-of-squares tree over v[0..P), P % 8 == 0. */
+/* The sum of squares of v[0..P), P % 8 == 0, in the order last set by
+ * oracle_set_ss_order (the wave64 tree unless set). */
 float oracle_sum_of_squares(const float* v, int P);
+void oracle_set_ss_order(int order);
+
+/* One route's normalization step by step, exposed for pinning:
+ * 1 / sqrt(ss * fp32(1/P) + eps), correctly rounded to FP32; and a BF16
+ * row x[P]'s weighted normalized FP32 products p[P] (gains
+ * fp32(gamma) + gain_center, the gain before or after the norm). */
+float oracle_inv_rms(float ss, int P, float eps);
+void oracle_route_products(const uint16_t* x, const uint16_t* gamma, float gain_center,
+                           float w, float eps, int weight_before_norm, int P, float* p);
 
 /* EP finalize: partials[tp][b][P] from rows[tp][R][P], idx[tp][b][K],
  * w[b][K] (FP32 or BF16), gamma[P]; out[b][P] (rank combine) if non-NULL. */

@@ -334,6 +334,35 @@ def test_upproj_unit_rows_and_zero_weights():
     assert np.array_equal(got_o, want)
 
 
+def test_upproj_two_unit_weights_per_row():
+    """out = bf16(y[a] + y[c]) from the BF16 normed row y, bit for bit with
+    the oracle (the sum of two BF16 products is exact in the FP32 sum)."""
+    inp = workloads.upproj(4, b=20, tp=4, L=544, N=128)
+    rng = np.random.default_rng(2)
+    a, c = rng.integers(0, 544, 128), rng.integers(0, 544, 128)
+    c = np.where(c == a, (c + 1) % 544, c)
+    w = np.zeros((128, 544), np.float32)
+    w[np.arange(128), a] = 1.0
+    w[np.arange(128), c] = 1.0
+    inp["w_up"] = bits(w)
+    _, want_o = oracle.combine_norm_upproj(inp["lat"], inp["gamma"], inp["eps"], inp["w_up"])
+    for layout in (mt.W_ROWS, mt.W_TILED):
+        _, got_o = run_upproj(inp, layout=layout)
+        assert np.array_equal(got_o, want_o)
+
+
+def test_upproj_golden_rs_after_the_k_sum():
+    case = json.load(open(os.path.join(GOLDEN, "upproj_rs_order.json")))["case"]
+    tp, b, L, N = case["tp"], case["b"], case["L"], case["N"]
+    w = np.zeros((N, L), np.float32)
+    w[:, 0], w[:, 1] = 2.0 ** 24, -2.0 ** 24
+    inp = dict(lat=bits(np.ones((tp, b, L))), gamma=bits(np.ones(L)), eps=case["eps"],
+               w_up=bits(w), b=b, tp=tp, L=L, N=N)
+    got_n, got_o = run_upproj(inp, rs=bits(np.ones((b, N))))
+    assert np.all(got_n == int(case["expected_normed_hex"], 16))
+    assert np.all(got_o == int(case["expected_out_hex"], 16))
+
+
 # ----------------------------------------------------------- shared expert --
 
 def run_shared(inp, with_h=True, layout=mt.W_ROWS):

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -16,6 +17,7 @@ import torch
 
 import oracle
 import workloads
+from tests import exact_ref as X
 from tests import fp64_ref as ref
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -74,11 +76,143 @@ def test_bf16_round_matches_fp64_definition():
 
 # -------------------------------------------------------- sum of squares --
 
-def test_sum_of_squares_golden_tree():
-    for case in golden("ss_tree.json")["cases"]:
+def _golden_row(case):
+    if "values" not in case:
         v = np.full(case["P"], case["rest"], np.float32)
         v[0] = case["v0"]
-        assert float(oracle.sum_of_squares(v)) == case["expected"]
+        return v
+    v = np.zeros(case["P"], np.float32)
+    for cols, val in case["values"].items():
+        lo, _, hi = cols.partition("..")
+        v[int(lo): int(hi or lo) + 1] = val
+    return v
+
+
+def test_sum_of_squares_golden_tree():
+    for case in golden("ss_tree.json")["cases"]:
+        assert float(oracle.sum_of_squares(_golden_row(case))) == case["expected"]
+
+
+def test_sum_of_squares_small_trees_exact():
+    """P = 8: lane 0 adds the 8 squares in column order, every other lane
+    holds 0.  P = 16: lanes 0 and 1 hold the ordered sums of columns 0..7
+    and 8..15, and the butterfly's first level adds them.  Checked in exact
+    arithmetic, each step rounded to FP32, on rows where the orders matter."""
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        v = (rng.standard_normal(16) * rng.choice([1.0, 1e3, 1e-3], 16)).astype(np.float32)
+        lanes = []
+        for lo in (0, 8):
+            s = Fraction(0)
+            for c in range(lo, lo + 8):
+                s = X.add(s, X.mul(Fraction(float(v[c])), Fraction(float(v[c]))))
+            lanes.append(s)
+        assert Fraction(float(oracle.sum_of_squares(v[:8]))) == lanes[0]
+        assert Fraction(float(oracle.sum_of_squares(v))) == X.add(lanes[0], lanes[1])
+
+
+def test_sum_of_squares_seq_order():
+    """The SEQ order is the plain column-order sum (the 2^24 golden row gives
+    2^24: every +1 after the first square ties back)."""
+    v = _golden_row(golden("ss_tree.json")["cases"][0])
+    with oracle.ss_order(oracle.SS_SEQ):
+        assert float(oracle.sum_of_squares(v)) == 2.0 ** 24
+        w = np.arange(1, 17, dtype=np.float32) * 1.37
+        s = Fraction(0)
+        for c in range(16):
+            s = X.add(s, X.mul(Fraction(float(w[c])), Fraction(float(w[c]))))
+        assert Fraction(float(oracle.sum_of_squares(w))) == s
+    assert float(oracle.sum_of_squares(v)) == 2.0 ** 24 + 504  # W64 again after the block
+
+
+# ---------------------------------------------------- inverse RMS ---------
+
+def _bits32(x):
+    return int(np.float32(x).view(np.uint32))
+
+
+def test_inv_rms_golden():
+    for case in golden("inv_rms.json")["cases"]:
+        ss = np.uint32(int(case["ss_hex"], 16)).view(np.float32)
+        assert float(ss) == case["ss"]
+        got = oracle.inv_rms(ss, case["P"], case["eps"])
+        assert _bits32(got) == int(case["expected_hex"], 16), case["what"]
+        # the derivation, redone in exact arithmetic, and the other reading
+        # really gives another value
+        m = X.add(X.mul(Fraction(float(ss)), X.rne(Fraction(1, case["P"]))), Fraction(case["eps"]))
+        assert X.f32_bits(X.rsqrt(m)) == int(case["expected_hex"], 16)
+        ((reading, other),) = case["other_reading"].items()
+        if reading.startswith("ss / P"):
+            alt = X.rsqrt(X.add(X.div(Fraction(float(ss)), case["P"]), Fraction(case["eps"])))
+        else:
+            alt = X.div(1, X.sqrt(m))
+        assert X.f32_bits(alt) == int(other, 16) != int(case["expected_hex"], 16)
+
+
+@pytest.mark.parametrize("P", [512, 520, 3584, 7168])
+def test_inv_rms_exact(P):
+    """1/sqrt(ss * fp32(1/P) + eps) with each step rounded to FP32 and the
+    reciprocal square root correctly rounded, in exact arithmetic."""
+    rng = np.random.default_rng(P)
+    ss = (rng.uniform(0.5, 2.0, 150) * P * rng.choice([1.0, 4.0, 0.01], 150)).astype(np.float32)
+    inv_p = X.rne(Fraction(1, P))
+    for eps in (0.0, 1e-6):
+        e = Fraction(float(np.float32(eps)))
+        for s in ss:
+            m = X.add(X.mul(Fraction(float(s)), inv_p), e)
+            assert _bits32(oracle.inv_rms(s, P, eps)) == X.f32_bits(X.rsqrt(m))
+
+
+# ---------------------------------------------- normalized route products --
+
+def _bf16_of(vals):
+    return oracle.bf16_round(np.asarray(vals, np.float32))
+
+
+def test_route_products_golden():
+    case = golden("route_products.json")["case"]
+    x = _bf16_of(case["x"])
+    gamma = np.full(case["P"], int(case["gamma_hex"], 16), np.uint16)
+    for key, wbn in (("gain_after", False), ("gain_first", True)):
+        got = oracle.route_products(x, gamma, case["gain_center"], case["w"], case["eps"], wbn)
+        want = [int(h, 16) for h in case[key]["expected_hex"]]
+        assert [_bits32(p) for p in got] == want, key
+        assert int(case[key]["other_order_col0_hex"], 16) != want[0]
+
+
+def _exact_route_products(x, gamma, gc, w, eps, wbn):
+    """The page order, each step rounded to FP32 (rows of 8 or 16 columns:
+    the sum of squares is the P = 8 / 16 tree of the test above)."""
+    P = len(x)
+    xs = [X.bf16_value(int(h)) for h in x]
+    g = [X.add(X.bf16_value(int(h)), Fraction(float(np.float32(gc)))) for h in gamma]
+    v = [X.mul(a, b) for a, b in zip(xs, g)] if wbn else xs
+    lanes = []
+    for lo in range(0, P, 8):
+        s = Fraction(0)
+        for c in range(lo, lo + 8):
+            s = X.add(s, X.mul(v[c], v[c]))
+        lanes.append(s)
+    ss = lanes[0] if P == 8 else X.add(lanes[0], lanes[1])
+    inv = X.rsqrt(X.add(X.mul(ss, X.rne(Fraction(1, P))), Fraction(float(np.float32(eps)))))
+    wf = Fraction(float(np.float32(w)))
+    if wbn:
+        return [X.mul(X.mul(v[c], inv), wf) for c in range(P)]
+    return [X.mul(X.mul(X.mul(xs[c], inv), g[c]), wf) for c in range(P)]
+
+
+@pytest.mark.parametrize("wbn", [False, True])
+def test_route_products_exact(wbn):
+    rng = np.random.default_rng(41 + wbn)
+    for P in (8, 16):
+        for _ in range(60):
+            x = bits(rng.standard_normal(P) * 2.0)
+            gamma = bits(rng.standard_normal(P) * 0.3)
+            gc = float(rng.choice([0.0, 1.0]))
+            w = float(np.float32(rng.uniform(0.01, 1.0)))
+            got = oracle.route_products(x, gamma, gc, w, 1e-6, wbn)
+            want = _exact_route_products(x, gamma, gc, w, 1e-6, wbn)
+            assert [_bits32(p) for p in got] == [X.f32_bits(p) for p in want]
 
 
 @pytest.mark.parametrize("P", [8, 64, 512, 520, 1032, 3584, 7168])
@@ -388,6 +522,84 @@ def test_upproj_random_vs_fp64_matmul():
     assert ref.within(out, exact, E).all()
     # a transposed or shifted operand is far outside
     assert not ref.within(out, y @ np.roll(W, 1, axis=1).T, E).all()
+
+
+def test_upproj_rs_after_the_k_sum_golden():
+    case = golden("upproj_rs_order.json")["case"]
+    tp, b, L, N = case["tp"], case["b"], case["L"], case["N"]
+    lat = bits(np.ones((tp, b, L)))
+    gamma = bits(np.ones(L))
+    w = np.zeros((N, L), np.float32)
+    w[:, 0], w[:, 1] = 2.0 ** 24, -2.0 ** 24
+    rs = bits(np.ones((b, N)))
+    normed, out = oracle.combine_norm_upproj(lat, gamma, case["eps"], bits(w), rs)
+    assert hexes(normed) == [case["expected_normed_hex"][2:]] * L
+    assert hexes(out) == [case["expected_out_hex"][2:]] * N
+
+
+def test_upproj_y_is_rounded_before_the_projection():
+    """Rows with two unit weights: out = bf16(y[a] + y[b]) where y is the
+    BF16 normed row (the sum of two BF16 values is exact in FP64); with y
+    left in FP32 most outputs would differ."""
+    inp = workloads.upproj(4, b=3, tp=4, L=544, N=96)
+    rng = np.random.default_rng(2)
+    a, c = rng.integers(0, 544, 96), rng.integers(0, 544, 96)
+    c = np.where(c == a, (c + 1) % 544, c)
+    w = np.zeros((96, 544), np.float32)
+    w[np.arange(96), a] = 1.0
+    w[np.arange(96), c] = 1.0
+    normed, out = oracle.combine_norm_upproj(inp["lat"], inp["gamma"], inp["eps"], bits(w))
+    y = ref.f64(normed)
+    want = oracle.bf16_round(ref.round_bf16(y[:, a] + y[:, c]).astype(np.float32))
+    assert np.array_equal(out, np.where(want == 0x8000, 0, want))
+
+
+# -------------------------------------------- the sum-of-squares order -----
+#
+# The plain sequential sum of squares (SEQ) against the wave64 tree (W64).
+# A different order moves an inverse RMS by an FP32 step now and then; where
+# a token's route products nearly cancel, that step is many BF16 steps of the
+# small result.  So between two orders the bar is: nearly every word
+# identical, and every word within the FP32 noise of its terms (32 u times
+# the sum of the products' magnitudes) plus one BF16 step -- not within one
+# BF16 step of the result itself.  Measured at decode scale: partials
+# 99.95-99.98% identical, the combined row 99.89% (gain after the norm) and
+# 99.98% (gain first).
+
+
+def _identical(a, b):
+    return float(np.mean(np.asarray(a) == np.asarray(b)))
+
+
+@pytest.mark.parametrize("wbn", [True, False])
+def test_ss_order_seq_against_w64_decode_scale(wbn):
+    inp = workloads.ep_finalize(0)
+    args = (inp["rows"], inp["idx"], inp["w32"], inp["gamma"], inp["gain_center"], inp["eps"], wbn)
+    p64, o64 = oracle.finalize(*args)
+    with oracle.ss_order(oracle.SS_SEQ):
+        pseq, oseq = oracle.finalize(*args)
+    _, scale = ref.ep_finalize(*args)
+    E = 32 * U24 * scale
+    assert ref.within(pseq, ref.f64(p64), E).all()
+    assert _identical(pseq, p64) >= 0.999
+    # the combine adds tp partials, each of which may sit one step apart
+    E_out = (E + ref.ulp_bf16(ref.f64(p64))).sum(axis=0)
+    assert ref.within(oseq, ref.f64(o64), E_out).all()
+    assert _identical(oseq, o64) >= 0.998
+    assert not np.array_equal(p64, pseq)  # the orders do differ somewhere
+
+
+def test_ss_order_seq_against_w64_expert_tp():
+    """Expert TP (K=16, P=7168, tp=8; 32 of the 128 tokens)."""
+    inp = workloads.tp_finalize(0, b=32)
+    args = (inp["kpart"], inp["idx"], inp["w32"], inp["gamma"], 0.0, inp["eps"], False)
+    o64 = oracle.tp_finalize(*args)
+    with oracle.ss_order(oracle.SS_SEQ):
+        oseq = oracle.tp_finalize(*args)
+    _, scale = ref.tp_finalize(*args)
+    assert ref.within(oseq, ref.f64(o64), 32 * U24 * scale).all()
+    assert _identical(oseq, o64) >= 0.999
+    assert not np.array_equal(o64, oseq)
 
 
 # ----------------------------------------------------------- shared expert --

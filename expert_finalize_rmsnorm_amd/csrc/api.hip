@@ -7,8 +7,8 @@
 // launches).
 #include "moetail.h"
 
-#include <stdio.h>
-#include <stdlib.h>
+#include <atomic>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -40,22 +40,10 @@ bool layout_ok(int w_layout) {
   return w_layout == MOETAIL_W_ROWS || w_layout == MOETAIL_W_TILED;
 }
 
-// The library's projection plans, with optional overrides read from the
-// environment at every call (tuning runs): MOETAIL_<KIND>_SPLITS, _WAVES,
-// _BLOCKS, _MR, _PF and _PASSES for KIND in UPPROJ, GATEUP, DOWN.  An override
-// that names no built kernel shape, or a slice that does not fit, is ignored.
-// Passes: 0 (the default) lets the plan choose, 1 is one LDS slice per
-// split, 2 or more that many slices per split.
-int env_int(const char* kind, const char* knob) {
-  char name[64];
-  snprintf(name, sizeof name, "MOETAIL_%s_%s", kind, knob);
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
-}
-ProjTuning tuning(const char* kind) {
-  return ProjTuning{env_int(kind, "SPLITS"), env_int(kind, "WAVES"), env_int(kind, "BLOCKS"),
-                    env_int(kind, "MR"), env_int(kind, "PF"), env_int(kind, "PASSES")};
-}
+// Projection kinds of moetail_set_projection_tuning, and the overrides set
+// through it (all zeros: the library's own plan).  Read under plan_mutex.
+ProjTuning tunings[3];
+std::mutex plan_mutex;
 
 // The expert-TP path keeps its rank-summed route rows [b][K][P] BF16, then
 // their sum-of-squares block totals [b][K][ceil(P/512)] FP32.
@@ -71,7 +59,7 @@ struct UpprojLayout {
 };
 UpprojLayout upproj_layout(int b, int L, int N) {
   UpprojLayout l;
-  l.plan = plan_projection(b, N, L, false, tuning("UPPROJ"));
+  l.plan = plan_projection(b, N, L, false, tunings[MOETAIL_PROJ_UPPROJ]);
   l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
   l.part_bytes = round_up(proj_partial_bytes(l.plan, b, N, false), 256);
   return l;
@@ -83,8 +71,8 @@ struct SharedLayout {
 };
 SharedLayout shared_layout(int b, int H, int I) {
   SharedLayout l;
-  l.gate_up = plan_projection(b, 2 * I, H, true, tuning("GATEUP"));
-  l.down = plan_projection(b, H, I, false, tuning("DOWN"));
+  l.gate_up = plan_projection(b, 2 * I, H, true, tunings[MOETAIL_PROJ_GATEUP]);
+  l.down = plan_projection(b, H, I, false, tunings[MOETAIL_PROJ_DOWN]);
   l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
   const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I, true);
   const size_t d = proj_partial_bytes(l.down, b, H, false);
@@ -102,9 +90,9 @@ struct TailLayout {
 // partials, since the last launch forms rs and then out.
 TailLayout tail_layout(int b, int L, int H, int I) {
   TailLayout l;
-  l.gate_up = plan_projection(b, 2 * I, H, true, tuning("GATEUP"));
-  l.down = plan_projection(b, H, I, false, tuning("DOWN"));
-  l.up = plan_projection(b, H, L, false, tuning("UPPROJ"));
+  l.gate_up = plan_projection(b, 2 * I, H, true, tunings[MOETAIL_PROJ_GATEUP]);
+  l.down = plan_projection(b, H, I, false, tunings[MOETAIL_PROJ_DOWN]);
+  l.up = plan_projection(b, H, L, false, tunings[MOETAIL_PROJ_UPPROJ]);
   l.group = (l.down.splits && l.up.splits) ? plan_group(b, l.down, H, l.up, H) : GroupPlan{};
   l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
   l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
@@ -116,6 +104,53 @@ TailLayout tail_layout(int b, int L, int H, int I) {
 }
 bool tail_ok(const TailLayout& l) {
   return l.gate_up.splits && l.down.splits && l.up.splits && l.group.waves;
+}
+
+// Plans are searched once per (operation, sizes, CU count, overrides) and
+// kept: the entry points look theirs up instead of searching on every call
+// (the [tail] BoundTail.run picks a kernel compiled once per set of
+// constants).  A fixed table of the last kPlanSlots shapes, guarded by
+// plan_mutex; a change of overrides empties it.
+constexpr int kPlanSlots = 64;
+struct PlanSlot {
+  bool used;
+  int op, b, d0, d1, d2, cu;
+  UpprojLayout up;
+  SharedLayout sh;
+  TailLayout tail;
+};
+PlanSlot plan_slots[kPlanSlots];
+int plan_next = 0;
+std::atomic<uint64_t> plan_searches{0}, plan_hits{0};
+
+// The layouts of one operation's call (the member for `op` is filled).
+PlanSlot plans_for(int op, int b, int d0, int d1, int d2) {
+  const int cu = device_cu_count();
+  std::lock_guard<std::mutex> lock(plan_mutex);
+  for (const PlanSlot& e : plan_slots)
+    if (e.used && e.op == op && e.b == b && e.d0 == d0 && e.d1 == d1 && e.d2 == d2 && e.cu == cu) {
+      plan_hits.fetch_add(1, std::memory_order_relaxed);
+      return e;
+    }
+  plan_searches.fetch_add(1, std::memory_order_relaxed);
+  PlanSlot e{};
+  e.used = true;
+  e.op = op, e.b = b, e.d0 = d0, e.d1 = d1, e.d2 = d2, e.cu = cu;
+  if (op == MOETAIL_OP_COMBINE_NORM_UPPROJ) e.up = upproj_layout(b, d0, d1);
+  if (op == MOETAIL_OP_SHARED_EXPERT) e.sh = shared_layout(b, d0, d1);
+  if (op == MOETAIL_OP_TAIL) e.tail = tail_layout(b, d0, d1, d2);
+  plan_slots[plan_next] = e;
+  plan_next = (plan_next + 1) % kPlanSlots;
+  return e;
+}
+UpprojLayout upproj_plan(int b, int L, int N) {
+  return plans_for(MOETAIL_OP_COMBINE_NORM_UPPROJ, b, L, N, 0).up;
+}
+SharedLayout shared_plan(int b, int H, int I) {
+  return plans_for(MOETAIL_OP_SHARED_EXPERT, b, H, I, 0).sh;
+}
+TailLayout tail_plan(int b, int L, int H, int I) {
+  return plans_for(MOETAIL_OP_TAIL, b, L, H, I).tail;
 }
 
 }  // namespace
@@ -176,7 +211,7 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const u
   if (L % 32 || L > MOETAIL_MAX_WIDTH || N % 64 || tp > MOETAIL_MAX_TP ||
       b > MOETAIL_MAX_GEMM_TOKENS)
     return MOETAIL_EUNSUPPORTED;
-  const UpprojLayout lay = upproj_layout(b, L, N);
+  const UpprojLayout lay = upproj_plan(b, L, N);
   if (lay.plan.splits == 0) return MOETAIL_EUNSUPPORTED;
   const size_t need = (normed ? 0 : lay.y_bytes) + lay.part_bytes;
   if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
@@ -200,7 +235,7 @@ int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gat
   if (H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
       b > MOETAIL_MAX_GEMM_TOKENS)
     return MOETAIL_EUNSUPPORTED;
-  const SharedLayout lay = shared_layout(b, H, I);
+  const SharedLayout lay = shared_plan(b, H, I);
   if (lay.gate_up.splits == 0 || lay.down.splits == 0) return MOETAIL_EUNSUPPORTED;
   const size_t need = (h ? 0 : lay.h_bytes) + lay.part_bytes;
   if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
@@ -231,7 +266,7 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
   if (L % 32 || L > MOETAIL_MAX_WIDTH || H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K ||
       I > MOETAIL_MAX_GEMM_K || tp > MOETAIL_MAX_TP || b > MOETAIL_MAX_GEMM_TOKENS)
     return MOETAIL_EUNSUPPORTED;
-  const TailLayout lay = tail_layout(b, L, H, I);
+  const TailLayout lay = tail_plan(b, L, H, I);
   if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
   const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
   if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
@@ -292,7 +327,7 @@ int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank, const int32
   if (L % 32 || H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
       b > MOETAIL_MAX_GEMM_TOKENS)
     return MOETAIL_EUNSUPPORTED;
-  const TailLayout lay = tail_layout(b, L, H, I);
+  const TailLayout lay = tail_plan(b, L, H, I);
   if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
   const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
   if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
@@ -329,26 +364,42 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
     case MOETAIL_OP_COMBINE_NORM_UPPROJ: {
       if (dim0 <= 0 || dim1 <= 0 || dim0 % 32 || dim1 % 64 || dim0 > MOETAIL_MAX_WIDTH) return 0;
       (void)dim2;
-      const UpprojLayout l = upproj_layout(b, dim0, dim1);
+      const UpprojLayout l = upproj_plan(b, dim0, dim1);
       return l.plan.splits ? l.y_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_TAIL: {
       if (dim0 <= 0 || dim1 <= 0 || dim2 <= 0 || dim0 % 32 || dim0 > MOETAIL_MAX_WIDTH ||
           dim1 % 64 || dim2 % 64 || dim1 > MOETAIL_MAX_GEMM_K || dim2 > MOETAIL_MAX_GEMM_K)
         return 0;
-      const TailLayout l = tail_layout(b, dim0, dim1, dim2);
+      const TailLayout l = tail_plan(b, dim0, dim1, dim2);
       return tail_ok(l) ? l.h_bytes + l.y_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_SHARED_EXPERT: {
       if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64 || dim0 > MOETAIL_MAX_GEMM_K ||
           dim1 > MOETAIL_MAX_GEMM_K)
         return 0;
-      const SharedLayout l = shared_layout(b, dim0, dim1);
+      const SharedLayout l = shared_plan(b, dim0, dim1);
       return l.gate_up.splits && l.down.splits ? l.h_bytes + l.part_bytes : 0;
     }
     default:
       return 0;
   }
+}
+
+int moetail_set_projection_tuning(int kind, int splits, int waves, int blocks, int tiles_per_unit,
+                                  int prefetch, int passes) {
+  if (kind < MOETAIL_PROJ_UPPROJ || kind > MOETAIL_PROJ_DOWN) return MOETAIL_EINVAL;
+  if (splits < 0 || waves < 0 || blocks < 0 || tiles_per_unit < 0 || prefetch < 0 || passes < 0)
+    return MOETAIL_EINVAL;
+  std::lock_guard<std::mutex> lock(plan_mutex);
+  tunings[kind] = ProjTuning{splits, waves, blocks, tiles_per_unit, prefetch, passes};
+  for (PlanSlot& e : plan_slots) e.used = false;  // plans made under the old overrides
+  return MOETAIL_OK;
+}
+
+void moetail_plan_cache_stats(uint64_t* searches, uint64_t* hits) {
+  if (searches) *searches = plan_searches.load(std::memory_order_relaxed);
+  if (hits) *hits = plan_hits.load(std::memory_order_relaxed);
 }
 
 const char* moetail_status_string(int status) {

@@ -32,6 +32,8 @@
 //    and down projections run that way.
 // Results are deterministic: the slice sum order is fixed and each slice is
 // one wave's in-order MFMA chain, whichever block runs it.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "norm_device.h"
@@ -810,15 +812,26 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   return p;  // splits == 0: no slice of K fits the LDS
 }
 
+// A kernel may take the whole LDS: set once per device (the setting is the
+// same every time; a bit per device in `done` keeps the call off later
+// launches, and concurrent first calls just set it twice).
+hipError_t allow_full_lds(const void* fn, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <int NT, int MR, int PF, int W, int H>
 hipError_t px_launch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
-  static bool attr_set = false;  // idempotent: every call sets the same maximum
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_kernel<NT, MR, PF, W, H>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_kernel<NT, MR, PF, W, H>), lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((px_kernel<NT, MR, PF, W, H>), dim3(p.splits * p.blocks_per_slice),
                      dim3(kWave * W), p.lds, s, a);
   return hipGetLastError();
@@ -846,13 +859,9 @@ hipError_t px_dispatch_hold(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
 
 template <int NT, int W, int U>
 hipError_t mp_launch(const FxArgs& a0, const ProjPlan& p, hipStream_t s) {
-  static bool attr_set = false;  // idempotent: every call sets the same maximum
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_mp_kernel<NT, W, U>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(reinterpret_cast<const void*>(px_mp_kernel<NT, W, U>), lds_set);
+  if (e != hipSuccess) return e;
   FxArgs a = a0;
   a.passes = p.passes;
   hipLaunchKernelGGL((px_mp_kernel<NT, W, U>), dim3(p.splits * p.blocks_per_slice),
@@ -919,13 +928,10 @@ hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
 template <int NT, int W, int H>
 hipError_t group_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks, size_t lds,
                         hipStream_t s) {
-  static bool attr_set = false;  // idempotent: every call sets the same maximum
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_group_kernel<NT, W, H>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_group_kernel<NT, W, H>), lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((px_group_kernel<NT, W, H>), dim3(blocks), dim3(kWave * W), lds, s, a0, a1,
                      blocks0);
   return hipGetLastError();
@@ -934,13 +940,10 @@ hipError_t group_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blo
 template <int NT, int W, int U>
 hipError_t group_mp_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
                            size_t lds, hipStream_t s) {
-  static bool attr_set = false;  // idempotent: every call sets the same maximum
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(px_group_mp_kernel<NT, W, U>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_group_mp_kernel<NT, W, U>), lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((px_group_mp_kernel<NT, W, U>), dim3(blocks), dim3(kWave * W), lds, s, a0,
                      a1, blocks0);
   return hipGetLastError();
@@ -986,18 +989,23 @@ hipError_t group_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks0, in
 
 }  // namespace
 
-// CUs of the current device (256 on MI355X), read once.
+// CUs of the current device (256 on MI355X), queried once per device; 256
+// when there is no device to ask (the host-side plan checks).
 int device_cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];  // zero: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const bool slot = dev >= 0 && dev < kMaxDevices;
+  if (slot) {
+    const int v = cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
   }
-  return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  if (slot) cus[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const ProjTuning& t) {

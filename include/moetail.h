@@ -68,6 +68,11 @@ extern "C" {
 #define MOETAIL_OP_SHARED_EXPERT 3
 #define MOETAIL_OP_TAIL 4
 
+/* Projection kinds of moetail_set_projection_tuning. */
+#define MOETAIL_PROJ_UPPROJ 0 /* the up projection (moetail_combine_norm_upproj, the tail's) */
+#define MOETAIL_PROJ_GATEUP 1 /* the shared expert's gate/up projection */
+#define MOETAIL_PROJ_DOWN 2   /* the shared expert's down projection */
+
 /* Limits.  P (and L) % 8 == 0 ([tail] 8-column fragments). */
 #define MOETAIL_MAX_WIDTH 8192  /* P, L: rows held in registers, 512 columns per wave */
 #define MOETAIL_MAX_TP 32       /* [tail] _TailReduceKernel: tp between 1 and 32 */
@@ -290,6 +295,35 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
  * Returns 0 for an unknown op or out-of-range sizes.
  */
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);
+
+/*
+ * Plan overrides for one projection kind, for measurement runs and tests
+ * only: every later call of this process (every device and stream) plans
+ * that projection with them.  Each knob 0 leaves the library's choice:
+ *   splits          K slices (their FP32 partials are added in slice order)
+ *   waves           waves per block (7, 8, 14, 16; 8 or 12 multi-pass)
+ *   blocks          blocks in the grid (default: one per CU)
+ *   tiles_per_unit  16-row tiles a wave streams together (1 or 2)
+ *   prefetch        k steps in flight per wave (4 or 8)
+ *   passes          LDS slices per split (1: one; 2 or more: multi-pass)
+ * All zeros restores the library's plan.  An override that names no built
+ * kernel shape, or whose slice does not fit the LDS, falls back to the
+ * library's plan.  The K slices fix the FP32 summation order, so an
+ * override changes the projection outputs' bits (within the same error
+ * bound); production callers never set one.  Setting is thread-safe; calls
+ * running meanwhile use either the old or the new plan.
+ * Returns MOETAIL_EINVAL for an unknown kind or a negative knob.
+ */
+int moetail_set_projection_tuning(int kind, int splits, int waves, int blocks,
+                                  int tiles_per_unit, int prefetch, int passes);
+
+/*
+ * Plan searches and plan-cache hits so far in this process.  The projection
+ * plans of a shape are searched once (per CU count and set of overrides) and
+ * looked up by every later call; diagnostics only.  Either pointer may be
+ * NULL.
+ */
+void moetail_plan_cache_stats(uint64_t* searches, uint64_t* hits);
 
 /* A static, human-readable text for a status code. */
 const char* moetail_status_string(int status);

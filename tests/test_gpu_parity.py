@@ -251,6 +251,19 @@ def test_tp_ragged_and_edges(b, K, P, tp, wbn):
     assert np.array_equal(got, want)
 
 
+def test_tp_no_norm_mode_is_refused_and_writes_nothing():
+    """The expert-TP finalize takes the two normalizing modes only: NO_NORM
+    reaches the library unchanged and is refused before any launch."""
+    tp = workloads.tp_finalize(0, b=4, K=4, P=1024, tp=4)
+    out = empty_bf16(4, 1024)
+    with pytest.raises(mt.MoetailError) as e:
+        mt.moetail_tp_finalize(dev(tp["kpart"]), dev(tp["idx"]), dev(tp["w32"]),
+                               dev(tp["gamma"]), 0.0, tp["eps"], mt.NO_NORM, out,
+                               workspace=mt.new_workspace(mt.OP_TP_FINALIZE, 4, 4, 1024))
+    assert e.value.status == mt.EINVAL
+    assert np.all(host(out) == SENTINEL)
+
+
 def test_tp_golden_round_before_norm():
     case = _golden("tp_round_before_norm.json")
     P = case["P"]
@@ -438,8 +451,27 @@ PLAN_OVERRIDES = [dict(WAVES=w, SPLITS=s) for w in (7, 8, 14, 16) for s in (2, 8
     dict(PASSES=2, BLOCKS=4), dict(PASSES=2, WAVES=12, BLOCKS=8)]
 
 
+_KIND = {"UPPROJ": mt.PROJ_UPPROJ, "GATEUP": mt.PROJ_GATEUP, "DOWN": mt.PROJ_DOWN}
+_KNOB = {"SPLITS": "splits", "WAVES": "waves", "BLOCKS": "blocks", "MR": "tiles_per_unit",
+         "PF": "prefetch", "PASSES": "passes"}
+
+
+def tuning_of(ov, kinds=None):
+    """{kind: knobs} for mt.projection_tuning from an override dict whose keys
+    are KNOB (for every kind in `kinds`) or KIND_KNOB."""
+    res = {}
+    for key, val in ov.items():
+        if "_" in key:
+            kind, knob = key.split("_", 1)
+            res.setdefault(_KIND[kind], {})[_KNOB[knob]] = val
+        else:
+            for kind in kinds:
+                res.setdefault(_KIND[kind], {})[_KNOB[key]] = val
+    return res
+
+
 @pytest.mark.parametrize("b", [1, 40, 128])
-def test_projection_plan_overrides(b, monkeypatch):
+def test_projection_plan_overrides(b):
     """Every kernel shape the plan can pick (waves per block, slice count,
     uneven blocks per slice, LDS passes per slice) against the oracle,
     through the tuning overrides; a slice count that does not fit falls back
@@ -451,21 +483,20 @@ def test_projection_plan_overrides(b, monkeypatch):
     want_h, want_rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
                                            nthreads=NT)
     for ov in PLAN_OVERRIDES:
-        for kind in ("UPPROJ", "GATEUP", "DOWN"):
-            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF", "PASSES"):
-                if key in ov:
-                    monkeypatch.setenv(f"MOETAIL_{kind}_{key}", str(ov[key]))
-                else:
-                    monkeypatch.delenv(f"MOETAIL_{kind}_{key}", raising=False)
-        _, got_up = run_upproj(up, rs=up["rs"])
-        gemm_bar(got_up, want_up, f"upproj b={b} {ov}")
-        got_h, got_rs = run_shared(sh)
-        gemm_bar(got_h, want_h, f"h b={b} {ov}")
-        gemm_bar(got_rs, want_rs, f"rs b={b} {ov}")
-        # the tiled weight layout: the same bits in every kernel shape
-        assert np.array_equal(run_upproj(up, rs=up["rs"], layout=mt.W_TILED)[1], got_up)
-        got_h2, got_rs2 = run_shared(sh, layout=mt.W_TILED)
-        assert np.array_equal(got_h2, got_h) and np.array_equal(got_rs2, got_rs)
+        with mt.projection_tuning(tuning_of(ov, ("UPPROJ", "GATEUP", "DOWN"))):
+            check_overridden_projections(b, ov, up, sh, want_up, want_h, want_rs)
+
+
+def check_overridden_projections(b, ov, up, sh, want_up, want_h, want_rs):
+    _, got_up = run_upproj(up, rs=up["rs"])
+    gemm_bar(got_up, want_up, f"upproj b={b} {ov}")
+    got_h, got_rs = run_shared(sh)
+    gemm_bar(got_h, want_h, f"h b={b} {ov}")
+    gemm_bar(got_rs, want_rs, f"rs b={b} {ov}")
+    # the tiled weight layout: the same bits in every kernel shape
+    assert np.array_equal(run_upproj(up, rs=up["rs"], layout=mt.W_TILED)[1], got_up)
+    got_h2, got_rs2 = run_shared(sh, layout=mt.W_TILED)
+    assert np.array_equal(got_h2, got_h) and np.array_equal(got_rs2, got_rs)
 
 
 def test_projections_graph_replay():
@@ -652,7 +683,7 @@ TAIL_OVERRIDES = [
 
 
 @pytest.mark.parametrize("b", [8, 40])
-def test_tail_plan_overrides(b, monkeypatch):
+def test_tail_plan_overrides(b):
     """The fused tail's grouped launch in its multi-pass form (either side
     multi-pass, the other run as one pass, with a shorter last slice) gives
     the bits of the two calls, and both match the oracle."""
@@ -664,14 +695,8 @@ def test_tail_plan_overrides(b, monkeypatch):
     want_o = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"], want_rs,
                                         nthreads=NT)[1]
     for ov in TAIL_OVERRIDES:
-        for kind in ("UPPROJ", "GATEUP", "DOWN"):
-            for key in ("WAVES", "SPLITS", "BLOCKS", "MR", "PF", "PASSES"):
-                name = f"{kind}_{key}"
-                if name in ov:
-                    monkeypatch.setenv(f"MOETAIL_{name}", str(ov[name]))
-                else:
-                    monkeypatch.delenv(f"MOETAIL_{name}", raising=False)
-        fused, calls = run_tail_and_calls(up, sh, layout=mt.W_TILED)
+        with mt.projection_tuning(tuning_of(ov)):
+            fused, calls = run_tail_and_calls(up, sh, layout=mt.W_TILED)
         for k in ("out", "rs", "normed", "h"):
             assert np.array_equal(fused[k], calls[k]), f"{k} {ov}"
         gemm_bar(fused["h"], want_h, f"tail h b={b} {ov}")

@@ -30,7 +30,7 @@ PROJ_UPPROJ, PROJ_GATEUP, PROJ_DOWN = 0, 1, 2  # projection kinds for set_projec
 
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
           "moetail_shared_expert", "moetail_tail", "moetail_decode_tail", "moetail_pack_weights",
-          "moetail_set_projection_tuning")
+          "moetail_set_projection_tuning", "moetail_decode_tail_noalloc")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string",
                          "moetail_plan_cache_stats")
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.moetail_set_projection_tuning.argtypes = [I32] * 7
         L.moetail_plan_cache_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)] * 2
         L.moetail_plan_cache_stats.restype = None
+        L.moetail_decode_tail_noalloc.argtypes = L.moetail_decode_tail.argtypes[:-3] + [P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
@@ -364,6 +365,37 @@ def moetail_decode_tail(rows, permuted_idx, route_w, fin_gamma, gain_center, fin
                                    _ptr(w_down), H, I, b, _ptr(out), _ptr(rs), _ptr(normed),
                                    _ptr(h), int(w_layout), ws, wsb, _stream(stream, dev))
     _check(st, "moetail_decode_tail")
+
+
+NOALLOC_SCRATCH_BYTES = 24 << 20  # the library's static scratch per GPU
+
+
+def moetail_decode_tail_noalloc(rows, permuted_idx, route_w, fin_gamma, gain_center, fin_eps,
+                                weight_before_norm, latent_partials, gamma, eps, w_up, x,
+                                w_gate, w_up_shared, w_down, out, rs=None, normed=None, h=None,
+                                stream=None, w_layout=W_ROWS):
+    """moetail_decode_tail without a workspace: the library's static scratch
+    (NOALLOC_SCRATCH_BYTES per GPU) serves instead, and the call allocates
+    nothing.  Calls on one GPU share that scratch and must not overlap."""
+    tp, b, L, H, I = _tail_shapes(latent_partials, gamma, w_up, x, w_gate, w_up_shared, w_down,
+                                  out, rs, normed, h)
+    if rows.dim() != 3 or permuted_idx.dim() != 3:
+        raise ValueError("rows must be [tp, R, L] and permuted_idx [tp, b, K]")
+    R = rows.shape[1]
+    K = permuted_idx.shape[2]
+    _expect(rows, "rows", (tp, R, L))
+    _index(permuted_idx, "permuted_idx", (tp, b, K))
+    _expect(route_w, "route_w", (b, K), _W_DTYPES)
+    _expect(fin_gamma, "fin_gamma", (L,), optional=True)
+    dev = _same_device(rows, permuted_idx, route_w, fin_gamma, latent_partials, gamma, w_up, x,
+                       w_gate, w_up_shared, w_down, out, rs, normed, h)
+    st = lib().moetail_decode_tail_noalloc(
+        _ptr(rows), R, _ptr(permuted_idx), _ptr(route_w), _weights(route_w), _ptr(fin_gamma),
+        float(gain_center), float(fin_eps), int(weight_before_norm), K, _ptr(latent_partials),
+        tp, _ptr(gamma), float(eps), _ptr(w_up), L, _ptr(x), _ptr(w_gate), _ptr(w_up_shared),
+        _ptr(w_down), H, I, b, _ptr(out), _ptr(rs), _ptr(normed), _ptr(h), int(w_layout),
+        _stream(stream, dev))
+    _check(st, "moetail_decode_tail_noalloc")
 
 
 def moetail_pack_weights(w, packed, stream=None):

@@ -12,6 +12,47 @@
 
 #include "kernels.h"
 
+// The allocation-free entry point's scratch (moetail_decode_tail_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` is only a stand-in for the symbol: its device
+// address on each GPU comes from hipGetSymbolAddress, looked up once per
+// device with that device current and kept in scratch_ptr; kernels get that
+// address, never the host name.
+constexpr size_t kScratchBytes = MOETAIL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+using namespace moetail;
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device
+
+// The scratch of the device that runs `stream` (the current device for the
+// null stream).  The first call on a device looks the address up with that
+// device current, then restores the caller's device.
+int scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MOETAIL_EHIP;
+  hipDevice_t dev = cur;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return MOETAIL_EHIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOETAIL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MOETAIL_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return MOETAIL_EHIP;
+    if (e != hipSuccess || p == nullptr) return MOETAIL_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return MOETAIL_OK;
+}
+
+}  // namespace
+
 namespace {
 
 using namespace moetail;
@@ -298,16 +339,20 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
   return hip_status(launch_pack_weights(w, n, k, packed, stream));
 }
 
-int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank, const int32_t* permuted_idx,
-                        const void* route_w, int route_w_dtype, const uint16_t* fin_gamma,
-                        float gain_center, float fin_eps, int weight_before_norm, int K,
-                        uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
-                        const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
-                        const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
-                        uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h,
-                        int w_layout, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
-  if (b == 0) return MOETAIL_OK;
+}  // extern "C"
+
+namespace {
+
+// moetail_decode_tail with its workspace; the allocation-free variant passes
+// this device's static scratch.
+int decode_tail_impl(const uint16_t* rows, int64_t rows_per_rank, const int32_t* permuted_idx,
+                     const void* route_w, int route_w_dtype, const uint16_t* fin_gamma,
+                     float gain_center, float fin_eps, int weight_before_norm, int K,
+                     uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
+                     const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
+                     const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
+                     uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h, int w_layout,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // the finalize's checks (P = L) ...
   if (weight_before_norm < MOETAIL_NORM_GAIN_AFTER || weight_before_norm > MOETAIL_NO_NORM)
     return MOETAIL_EINVAL;
@@ -350,6 +395,46 @@ int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank, const int32
   hipError_t e = launch_ep_finalize(ep, stream);
   if (e == hipSuccess) e = launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank, const int32_t* permuted_idx,
+                        const void* route_w, int route_w_dtype, const uint16_t* fin_gamma,
+                        float gain_center, float fin_eps, int weight_before_norm, int K,
+                        uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
+                        const uint16_t* w_up, int L, const uint16_t* x, const uint16_t* w_gate,
+                        const uint16_t* w_upw, const uint16_t* w_down, int H, int I, int b,
+                        uint16_t* out, uint16_t* rs, uint16_t* normed, uint16_t* h,
+                        int w_layout, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  return decode_tail_impl(rows, rows_per_rank, permuted_idx, route_w, route_w_dtype, fin_gamma,
+                          gain_center, fin_eps, weight_before_norm, K, latent_partials, tp, gamma,
+                          eps, w_up, L, x, w_gate, w_upw, w_down, H, I, b, out, rs, normed, h,
+                          w_layout, workspace, workspace_bytes, stream);
+}
+
+int moetail_decode_tail_noalloc(const uint16_t* rows, int64_t rows_per_rank,
+                                const int32_t* permuted_idx, const void* route_w,
+                                int route_w_dtype, const uint16_t* fin_gamma, float gain_center,
+                                float fin_eps, int weight_before_norm, int K,
+                                uint16_t* latent_partials, int tp, const uint16_t* gamma,
+                                float eps, const uint16_t* w_up, int L, const uint16_t* x,
+                                const uint16_t* w_gate, const uint16_t* w_upw,
+                                const uint16_t* w_down, int H, int I, int b, uint16_t* out,
+                                uint16_t* rs, uint16_t* normed, uint16_t* h, int w_layout,
+                                hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  void* ws = nullptr;
+  const int st = scratch_for(stream, &ws);
+  if (st) return st;
+  return decode_tail_impl(rows, rows_per_rank, permuted_idx, route_w, route_w_dtype, fin_gamma,
+                          gain_center, fin_eps, weight_before_norm, K, latent_partials, tp, gamma,
+                          eps, w_up, L, x, w_gate, w_upw, w_down, H, I, b, out, rs, normed, h,
+                          w_layout, ws, kScratchBytes, stream);
 }
 
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {

@@ -264,6 +264,36 @@ int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank,
                         hipStream_t stream);
 
 /*
+ * moetail_decode_tail without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same arguments but the workspace, the same
+ * kernels and the same bits.  Its scratch (the split partials, and h and y
+ * when not given) is a static device array of the library, one per GPU,
+ * MOETAIL_NOALLOC_SCRATCH_BYTES long, held until the process ends; the call
+ * allocates nothing.  A call whose sizes need more scratch than that (the
+ * workspace moetail_decode_tail would take, moetail_workspace_bytes(
+ * MOETAIL_OP_TAIL, b, L, H, I), beyond the maximum) returns
+ * MOETAIL_EWORKSPACE and enqueues nothing; at L = 3584, H = 7168,
+ * I = 6144 every b <= 64 fits (18.7 MiB at b = 64).  Every call on a GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams,
+ * other host threads) race and must not be issued; nothing in the scratch
+ * needs to start at zero.  The first call on a device looks the scratch's
+ * address up (make it before any graph capture).
+ */
+#define MOETAIL_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+int moetail_decode_tail_noalloc(const uint16_t* rows, int64_t rows_per_rank,
+                                const int32_t* permuted_idx, const void* route_w,
+                                int route_w_dtype, const uint16_t* fin_gamma,
+                                float gain_center, float fin_eps, int weight_before_norm,
+                                int K, uint16_t* latent_partials, int tp,
+                                const uint16_t* gamma, float eps, const uint16_t* w_up,
+                                int L, const uint16_t* x, const uint16_t* w_gate,
+                                const uint16_t* w_upw, const uint16_t* w_down, int H,
+                                int I, int b, uint16_t* out, uint16_t* rs,
+                                uint16_t* normed, uint16_t* h, int w_layout,
+                                hipStream_t stream);
+
+/*
  * The tiled copy of a weight matrix, made once when the weights are loaded
  * (weights are static at decode time).  The projections read either layout
  * (their w_layout argument) and give the same bits from both; the tiled one

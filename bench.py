@@ -41,7 +41,15 @@ B, P, TP, K = 64, 3584, 8, 16
 H, I = 7168, 6144
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-tail tokens/s and achieved HBM GB/s (% peak) at b=64, P=3584"
-GRAPH_STEPS = 8  # steps per captured graph
+MAX_GRAPH_STEPS = 40  # most steps per captured graph
+
+
+def graph_steps(steps: int) -> int:
+    """Steps per captured graph: the largest divisor of the step count up to
+    MAX_GRAPH_STEPS, so that every timed step sits in a graph of that size
+    (a decode loop holds many layers' tails in one graph; a replay boundary
+    costs about 8 us of launch, paid once per graph)."""
+    return max(g for g in range(1, min(steps, MAX_GRAPH_STEPS) + 1) if steps % g == 0)
 
 
 # HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
@@ -189,28 +197,23 @@ def main():
         main.wait_event(join)
         upproj(d)
 
-    log("capturing the step graphs")
+    log("capturing the step graph")
     for d in sets:
         step(d)  # eager once before capture
     torch.cuda.synchronize()
-    # One graph holds GRAPH_STEPS steps, the input sets alternating (a decode
-    # loop captures many layers' tails in one graph, so a replay boundary,
-    # about 8 us of launch, falls once per GRAPH_STEPS steps); the remainder
-    # of a step count runs as one-step graphs.
+    # One graph of G steps, the input sets alternating; the timed region
+    # replays it steps / G times (G divides the step count).
+    G = graph_steps(args.steps)
     cap = torch.cuda.Stream()
-    many, single = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    many = torch.cuda.CUDAGraph()
     with torch.cuda.graph(many, stream=cap):
-        for i in range(GRAPH_STEPS):
+        for i in range(G):
             step(sets[i % nsets])
-    with torch.cuda.graph(single, stream=cap):
-        step(sets[0])
     torch.cuda.synchronize()
 
     def run_steps(n):
-        for _ in range(n // GRAPH_STEPS):
+        for _ in range((n + G - 1) // G):
             many.replay()
-        for _ in range(n % GRAPH_STEPS):
-            single.replay()
 
     log(f"warmup {args.warmup}, timed {args.steps} steps")
     run_steps(args.warmup)
@@ -270,6 +273,9 @@ def main():
         log("copy calibration: 2 x neg over 268435456 B in, 268435456 B out")
         del src, dst
 
+    log("copy ceiling")
+    ceiling = copy_ceiling(step_bytes)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
@@ -288,6 +294,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
+        "graph_steps": G,
         "config": {"workload": "MoE decode tail step: EP finalize tp=8 K=16 P=3584 -> shared "
                                "expert 7168x6144 SiLU -> latent combine + RMSNorm + up "
                                "projection 3584->7168 (+rs)",
@@ -301,6 +308,8 @@ def main():
         "entry_points": entry,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "copy_ceiling": ceiling,
+        "targets": targets_of(kernels),
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -392,7 +401,7 @@ def config_kernels(base, log, lay):
     kp = [randn_bf16((8, 2048, 7168), 0.5) for _ in range(3)]
     tout = torch.empty((128, 7168), dtype=torch.int16, device="cuda")
     w, gamma = dev(w32), dev(tgamma)
-    tws = mt.new_workspace(mt.OP_TP_FINALIZE, 128, 16, 7168)
+    tws = mt.new_workspace(mt.OP_TP_FINALIZE, 128, 16, 7168, 8)
     us = timed(lambda i: mt.moetail_tp_finalize(kp[i], idx, w, gamma, 0.0, 1e-6, False, tout,
                                                 workspace=tws), 3, reps=12)
     add("tp_finalize b=128 K=16 P=7168 tp=8", us,
@@ -429,29 +438,109 @@ def config_kernels(base, log, lay):
     return res
 
 
-def cpu_baseline(host_inputs, log, min_seconds=10.0):
-    """The oracle (as it stands) on the step's full b=64 batch, on host
-    cores: whole steps repeated until at least min_seconds have passed."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def host_threads():
+    """The threads this process may use: the host's CPUs, capped by the
+    OpenMP thread setting where one is given (on a shared GPU host that is
+    this GPU's share of the cores)."""
+    n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def cpu_baseline(host_inputs, log, seconds=(8.0, 10.0)):
+    """The oracle (as it stands) on the step's full b=64 batch on host cores:
+    whole steps repeated until the time given has passed, once on one thread
+    and once on host_threads() threads (the results do not depend on the
+    thread count)."""
     import oracle
     ep, up, sh = host_inputs
-    threads = max(1, min(16, os.cpu_count() or 1))
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        lat, _ = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6, True,
-                                 combine=False, nthreads=threads)
-        _, rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
-                                     nthreads=threads)
-        oracle.combine_norm_upproj(lat, up["gamma"], 1e-6, up["w_up"], rs, nthreads=threads)
-        steps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    log(f"oracle: {steps} steps in {dt:.2f} s on {threads} threads")
-    return {"value": round(steps * B / dt, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{steps} full b={B} steps (finalize, shared expert, combine+norm+upproj) "
-                      f"of input set 0, {dt:.2f} s wall on {threads} threads"}
+
+    def run(threads, min_seconds):
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            lat, _ = oracle.finalize(ep["rows"], ep["idx"], ep["w32"], ep["gamma"], 1.0, 1e-6,
+                                     True, combine=False, nthreads=threads)
+            _, rs = oracle.shared_expert(sh["x"], sh["w_gate"], sh["w_up"], sh["w_down"],
+                                         nthreads=threads)
+            oracle.combine_norm_upproj(lat, up["gamma"], 1e-6, up["w_up"], rs, nthreads=threads)
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                return steps, dt
+
+    n = host_threads()
+    s1, t1 = run(1, seconds[0])
+    log(f"oracle: {s1} steps in {t1:.2f} s on 1 thread")
+    sn, tn = run(n, seconds[1])
+    log(f"oracle: {sn} steps in {tn:.2f} s on {n} threads")
+    return {"value": round(sn * B / tn, 2), "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{sn} full b={B} steps (finalize, shared expert, combine+norm+upproj) of "
+                      f"input set 0, {tn:.2f} s wall on {n} threads",
+            "single_thread": {"value": round(s1 * B / t1, 2), "unit": "tokens/s", "cores": 1,
+                              "sample": f"{s1} full b={B} steps, {t1:.2f} s wall on 1 thread"},
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def copy_ceiling(nbytes, reps=10):
+    """A device-to-device copy of nbytes (read nbytes, write nbytes), HIP
+    events around one replay of a graph of reps copies: the bandwidth a
+    plain copy reaches on this GPU, as the practical ceiling beside the
+    8 TB/s peak."""
+    import torch
+    n = nbytes // 2
+    src = [torch.empty(n, dtype=torch.int16, device="cuda").fill_(1) for _ in range(2)]
+    dst = torch.empty(n, dtype=torch.int16, device="cuda")
+    us = graph_time(lambda i: dst.copy_(src[i % 2]), reps)
+    del src, dst
+    return {"bytes_copied": n * 2, "us": round(us, 2),
+            "GBps_read_plus_write": round(2 * n * 2 / us / 1e3, 1)}
+
+
+def targets_of(kernels):
+    """Each workload's figure against its target (finalize and combine: at
+    least 70% of the 8 TB/s peak; the up projection and the shared expert at
+    b=32: at least 60% of the weight-streaming roofline)."""
+    if not kernels:
+        return None
+    by = {k["name"]: k for k in kernels}
+    res = []
+
+    def frac_target(name, key):
+        k = by.get(key)
+        if k:
+            res.append(dict(name=name, measured_frac=k["frac"], target_frac=0.70,
+                            us=k["us"], met=k["frac"] >= 0.70))
+
+    def time_target(name, key, roof_us):
+        k = by.get(key)
+        if k:
+            res.append(dict(name=name, us=k["us"], target_us=round(roof_us / 0.6, 2),
+                            measured_frac=round(roof_us / k["us"], 4), target_frac=0.60,
+                            met=k["us"] <= roof_us / 0.6))
+
+    frac_target("EP finalize + combine (b=64, partials and out)",
+                "finalize+combine b=64 P=3584 tp=8 wbn=1")
+    frac_target("EP finalize, partials only (b=64)", "finalize b=64, partials only")
+    frac_target("expert-TP finalize (b=128, P=7168)", "tp_finalize b=128 K=16 P=7168 tp=8")
+    time_target("combine + norm + up projection b=32", "combine_norm_upproj b=32",
+                H * P * 2 / HBM_PEAK_GBPS / 1e3)
+    time_target("shared expert b=32", "shared_expert b=32", 3 * H * I * 2 / HBM_PEAK_GBPS / 1e3)
+    return res
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_uppro
           "moetail_shared_expert", "moetail_tail", "moetail_decode_tail", "moetail_pack_weights",
           "moetail_set_projection_tuning", "moetail_decode_tail_noalloc")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string",
-                         "moetail_plan_cache_stats")
+                         "moetail_plan_cache_stats", "moetail_set_tp_wait_limit")
 
 
 class MoetailError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moetail_set_projection_tuning.argtypes = [I32] * 7
         L.moetail_plan_cache_stats.argtypes = [ctypes.POINTER(ctypes.c_uint64)] * 2
         L.moetail_plan_cache_stats.restype = None
+        L.moetail_set_tp_wait_limit.argtypes = [I64]
+        L.moetail_set_tp_wait_limit.restype = None
         L.moetail_decode_tail_noalloc.argtypes = L.moetail_decode_tail.argtypes[:-3] + [P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
@@ -174,6 +176,12 @@ class projection_tuning:
         for kind in (PROJ_UPPROJ, PROJ_GATEUP, PROJ_DOWN):
             set_projection_tuning(kind)
         return False
+
+
+def set_tp_wait_limit(ticks: int = 2000000) -> None:
+    """The one-pass expert-TP finalize's wait limit (100 MHz ticks; < 0: no
+    wait, each block forms its partner's totals itself)."""
+    lib().moetail_set_tp_wait_limit(int(ticks))
 
 
 def plan_cache_stats():
@@ -419,9 +427,11 @@ def pack_weights(w, stream=None):
 
 
 def new_workspace(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0, device="cuda"):
-    """A device byte tensor sized for one call of `op` (None when none is needed)."""
+    """A device byte tensor sized for one call of `op` (None when none is
+    needed), zeroed (the expert-TP finalize needs its flags zero before the
+    first use; every call leaves them so)."""
     n = workspace_bytes(op, b, dim0, dim1, dim2)
     if n == 0:
         return None
     # the caching allocator hands out blocks aligned to at least 512 bytes
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)

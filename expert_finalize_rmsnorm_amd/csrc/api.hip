@@ -86,13 +86,29 @@ bool layout_ok(int w_layout) {
 ProjTuning tunings[3];
 std::mutex plan_mutex;
 
-// The expert-TP path keeps its rank-summed route rows [b][K][P] BF16, then
-// their sum-of-squares block totals [b][K][ceil(P/512)] FP32.
-size_t tp_rows_bytes(int b, int K, int P) { return round_up(sizeof(uint16_t) * (size_t)b * K * P, 256); }
-size_t tp_workspace(int b, int K, int P) {
-  return tp_rows_bytes(b, K, P) +
-         round_up(sizeof(float) * (size_t)b * K * ((P + 511) / 512), 256);  // 512-column blocks
+// The expert-TP workspace: the one-pass kernel's token generations [b]
+// (zero before the first use) and its tagged 512-column block totals
+// [b][16 or 32][ceil(P/512)] (64-bit words); then, for more than
+// kTpOnePassMaxRanks ranks (or tp unknown, 0), the two-pass path's
+// rank-summed route rows [b][K][P] BF16 and their sum-of-squares block
+// totals [b][K][ceil(P/512)] FP32.
+size_t tp_gen_bytes(int b) { return round_up(sizeof(unsigned) * (size_t)b, 256); }
+size_t tp_slot_bytes(int b, int K, int P) {
+  const int kslots = K <= 16 ? 16 : 32;  // the kernel's route capacity: every slot is written
+  return round_up(sizeof(uint64_t) * (size_t)b * kslots * ((P + 511) / 512), 256);
 }
+size_t tp_rows_bytes(int b, int K, int P) { return round_up(sizeof(uint16_t) * (size_t)b * K * P, 256); }
+size_t tp_workspace(int b, int K, int P, int tp) {
+  size_t n = tp_gen_bytes(b) + tp_slot_bytes(b, K, P);
+  if (tp <= 0 || tp > kTpOnePassMaxRanks)
+    n += tp_rows_bytes(b, K, P) +
+         round_up(sizeof(float) * (size_t)b * K * ((P + 511) / 512), 256);  // 512-column blocks
+  return n;
+}
+
+// The one-pass expert-TP kernel's wait limit for a block total (100 MHz
+// ticks; 20 ms; < 0: no wait, a wave forms the totals that are not there).
+std::atomic<long long> tp_wait_ticks{2000000};
 
 struct UpprojLayout {
   ProjPlan plan;
@@ -230,13 +246,16 @@ int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows, const int32
   if (!a16(kpartials) || num_rows <= 0 || permuted_idx == nullptr || !aligned(permuted_idx, 4) ||
       !a16(out) || !__builtin_isfinite(gain_center))
     return MOETAIL_EINVAL;
-  const size_t need = tp_workspace(b, K, P);
+  const size_t need = tp_workspace(b, K, P, tp);
   if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
     return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  char* rows = ws + tp_gen_bytes(b) + tp_slot_bytes(b, K, P);
   TpArgs a{kpartials, num_rows, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, gamma,
            gain_center, eps, weight_before_norm != 0, b, K, P, tp, out,
-           static_cast<uint16_t*>(workspace),
-           reinterpret_cast<float*>(static_cast<char*>(workspace) + tp_rows_bytes(b, K, P))};
+           reinterpret_cast<unsigned*>(ws), reinterpret_cast<uint64_t*>(ws + tp_gen_bytes(b)),
+           tp_wait_ticks.load(std::memory_order_relaxed), reinterpret_cast<uint16_t*>(rows),
+           reinterpret_cast<float*>(rows + tp_rows_bytes(b, K, P))};
   return hip_status(launch_tp_finalize(a, stream));
 }
 
@@ -442,7 +461,8 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
     if (b <= 0 || b > MOETAIL_MAX_TOKENS || dim0 <= 0 || dim0 > MOETAIL_MAX_ROUTES || dim1 <= 0 ||
         dim1 % 8 || dim1 > MOETAIL_MAX_WIDTH)
       return 0;
-    return tp_workspace(b, dim0, dim1);
+    if (dim2 < 0 || dim2 > MOETAIL_MAX_TP) return 0;
+    return tp_workspace(b, dim0, dim1, dim2);
   }
   if (b <= 0 || b > MOETAIL_MAX_GEMM_TOKENS) return 0;
   switch (op) {
@@ -480,6 +500,10 @@ int moetail_set_projection_tuning(int kind, int splits, int waves, int blocks, i
   tunings[kind] = ProjTuning{splits, waves, blocks, tiles_per_unit, prefetch, passes};
   for (PlanSlot& e : plan_slots) e.used = false;  // plans made under the old overrides
   return MOETAIL_OK;
+}
+
+void moetail_set_tp_wait_limit(int64_t ticks) {
+  tp_wait_ticks.store(ticks, std::memory_order_relaxed);
 }
 
 void moetail_plan_cache_stats(uint64_t* searches, uint64_t* hits) {

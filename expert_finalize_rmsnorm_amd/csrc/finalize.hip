@@ -451,6 +451,247 @@ __global__ void __launch_bounds__(256) tp_norm_kernel(const uint16_t* xr, const 
   store16(out + (int64_t)t * P + col, pack8_pz(acc));
 }
 
+// ------------------------------------------------ expert-TP in one pass --
+//
+// Two blocks per token (its columns in two halves of 512-column blocks),
+// one wave per 512 columns, so that the 235 MB of K-partials stream through
+// every CU (measured: a plain read of that size reaches 6.4 TB/s with 256
+// blocks of 7 waves, 5.4 TB/s with 128 blocks of 14).  x_r never leaves the
+// chip: a wave streams the routes in order, two routes' loads ahead, and
+// holds each route's rank sums only until that route's products are added.
+//
+// A route's inverse RMS needs the whole row's sum of squares, i.e. the
+// 512-column block totals of every wave of both blocks.  Each wave writes its
+// block total of route k, as soon as it has it, to a mailbox slot: one 64-bit
+// word (tag << 32 | FP32 bits), written and read whole, so no fence orders
+// it.  Two routes later the wave polls the row's slots of route k (the poll
+// issued before the next stream loads, read one route after), adds the totals
+// in column order from 0 (the same tree and bits as the two-pass path), and
+// adds route k's weighted normalized products.  The exchange overlaps the
+// stream instead of following it.
+//
+// The tag is the token's generation (read at the start, plus one); every
+// wave raises the generation to its tag at the end, so a later call's tag is
+// above every slot an earlier call left (the workspace is zero before its
+// first use).  A wait is bounded: a wave whose slots are not all there
+// within the limit forms the missing block totals itself from the
+// K-partials (slower, the same bits), and from then on waits no more.  No
+// barrier and no fence: no result depends on two blocks running at once.
+struct TpMailArgs {
+  const uint16_t* kpart;  // [tp][num_rows][P]
+  int64_t num_rows;
+  const int32_t* idx;     // [b][K]
+  const void* w;          // [b][K]
+  const uint16_t* gamma;  // [P]
+  float gain_center, eps;
+  int K, P, tp;
+  uint16_t* out;          // [b][P]
+  unsigned* gen;          // [b]: each token's generation
+  uint64_t* slots;        // [b][KMAX][ceil(P/512)]: (tag << 32) | FP32 block total
+                          // (KMAX = 16 for K <= 16, else 32; every slot written each call)
+  int wpb;                // waves per block: block x takes column blocks x * wpb ..
+  long long wait_ticks;   // wait limit in 100 MHz ticks; < 0: do not wait
+};
+
+// A row of zeros as wide as the widest row: the chunks of the ranks past tp.
+__device__ uint4 tp_zero_row[MOETAIL_MAX_WIDTH / kChunk];
+
+// One route's K-partial chunks of the 8 columns at colc, every rank's load
+// in flight (tp <= 8; ranks past tp read zeros, whose +0 changes no sum:
+// the sums start at +0 and are never -0).  Issued whether or not the route
+// is there -- an absent one reads the gamma chunk instead, a cache hit -- so
+// the loads in flight stay countable and the wait for one route never
+// drains the loads ahead of it.
+__device__ __forceinline__ void tp_issue(const TpMailArgs& a, bool there, int r, int colc,
+                                         uint4 (&q)[8]) {
+  const uint16_t* src = there ? a.kpart + (int64_t)r * a.P + colc : a.gamma + colc;
+  const int64_t rank_stride = there ? a.num_rows * (int64_t)a.P : 0;
+  const uint16_t* zeros = reinterpret_cast<const uint16_t*>(tp_zero_row) + colc;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) q[u] = load16_stream(u < a.tp ? src + u * rank_stride : zeros);
+}
+
+// x_r = bf16(sum over ranks, in rank order from +0).
+__device__ __forceinline__ uint4 tp_rank_sum(const uint4 (&q)[8]) {
+  float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float v[8];
+    unpack8(q[u], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+  }
+  return pack8(sum);
+}
+
+// The 512-column block total of route row r over column block jj, formed by
+// one wave from the K-partials (for a block total whose slot did not come).
+template <int MODE>
+__device__ __forceinline__ float tp_block_total(const TpMailArgs& a, int r, int jj) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = (jj * kWave + lane) * kChunk;
+  const bool has = col < a.P;
+  const int colc = has ? col : a.P - kChunk;
+  uint4 q[8];
+  tp_issue(a, true, r, colc, q);
+  float g[8];
+  unpack8(load16(a.gamma + colc), g);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) g[c] = g[c] + a.gain_center;
+  const uint4 x = tp_rank_sum(q);
+  return wave_butterfly_sum(has ? chunk_ss<MODE>(x, g) : 0.0f);
+}
+
+// The slow path of a poll: the slots of one route (ms[0 .. nbk)) that are
+// not there are read again until `limit` ticks have passed (then `limit`
+// becomes -1: no more waiting), and any still missing are formed from the
+// K-partials of route row r.  v: this lane's read of slot `lane`; returns
+// the lane's slot as a complete read has it.
+template <int MODE>
+__device__ __forceinline__ uint64_t tp_wait_slots(const TpMailArgs& a, const uint64_t* ms,
+                                                  int nbk, unsigned tag, int r, uint64_t v,
+                                                  long long& limit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool ready = lane >= nbk || (unsigned)(v >> 32) == tag;
+  if (limit >= 0) {
+    const long long t0 = wall_clock64();
+    while (__ballot(!ready)) {
+      if (wall_clock64() - t0 > limit) {
+        limit = -1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      if (!ready) {
+        v = __hip_atomic_load(ms + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ready = (unsigned)(v >> 32) == tag;
+      }
+    }
+  }
+  uint64_t missing = __ballot(!ready);
+  while (missing) {
+    const int jj = __builtin_ctzll(missing);
+    missing &= missing - 1;
+    const float tot = tp_block_total<MODE>(a, r, jj);
+    if (lane == jj) v = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(tot);
+  }
+  return v;
+}
+
+constexpr int kTpMaxAhead = 4;  // most routes a wave's loads run ahead
+
+// A wave's state through the stream: route k's loads in q[k % (ahead + 1)], its rank
+// sums in xr[k] until its products are added, the FP32 sums, and the slot
+// read polled last.
+template <int KMAX>
+struct TpWave {
+  int lane, j, col, colc, nbk, e;
+  bool has;
+  float wk;
+  uint64_t present;
+  unsigned tag;
+  uint64_t* tslots;
+  long long limit;
+  float g[8];
+  uint4 q[kTpMaxAhead + 1][8];  // route k's loads in q[k % (ahead + 1)]
+  uint4 xr[KMAX];
+  float acc[8];
+  uint64_t poll;
+};
+
+// Step k of the stream (template recursion, so every k is a constant and the
+// state stays in registers): poll route k - kLag, issue route k + kAhead's
+// loads, add route k's ranks and publish its block total, then add route
+// k - kLag - 1's products (its poll came in with route k's loads).
+template <int MODE, int KMAX, int kAhead, int k>
+__device__ __forceinline__ void tp_step(const TpMailArgs& a, TpWave<KMAX>& w) {
+  constexpr int kLag = 2;    // routes between a slot's write and its poll
+  // Every memory operation below is issued on every path (routes that are
+  // not there use stand-in data and a slot of their own): only arithmetic
+  // depends on which routes are there.
+  constexpr int mp = k - kLag;
+  uint64_t next_poll = 0;
+  if (mp >= 0 && mp < KMAX)
+    next_poll = __hip_atomic_load(w.tslots + (int64_t)(mp < 0 ? 0 : mp) * w.nbk +
+                                      min(w.lane, w.nbk - 1),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (k + kAhead < KMAX) {
+    constexpr int kn = k + kAhead < KMAX ? k + kAhead : 0;
+    tp_issue(a, (w.present >> kn) & 1ull, readlane_i(w.e, kn), w.colc, w.q[kn % (kAhead + 1)]);
+  }
+  if (k < KMAX) {
+    constexpr int kk = k < KMAX ? k : 0;
+    const uint4 x = tp_rank_sum(w.q[kk % (kAhead + 1)]);
+    w.xr[kk] = x;
+    const float tot = wave_butterfly_sum(w.has ? chunk_ss<MODE>(x, w.g) : 0.0f);
+    // lane 0 stores the wave's total (64 lanes writing one word would be 64
+    // writes; one lane's store under the exec mask is still counted)
+    if (w.lane == 0)
+      __hip_atomic_store(w.tslots + (int64_t)kk * w.nbk + w.j,
+                         ((uint64_t)w.tag << 32) | (uint64_t)__float_as_uint(tot),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  constexpr int m = k - kLag - 1;
+  if (m >= 0 && m < KMAX && ((w.present >> (m < 0 ? 0 : m)) & 1ull)) {
+    constexpr int mm = m < 0 ? 0 : m;
+    uint64_t v = w.poll;
+    const bool ready = (unsigned)(v >> 32) == w.tag;
+    if (__ballot(!ready))
+      v = tp_wait_slots<MODE>(a, w.tslots + (int64_t)mm * w.nbk, w.nbk, w.tag,
+                              readlane_i(w.e, mm), v, w.limit);
+    const float mine = __uint_as_float((unsigned)v);
+    float total = 0.0f;  // block totals in column order from 0
+#pragma unroll
+    for (int jj = 0; jj < MOETAIL_MAX_WIDTH / kBlockCols; ++jj)
+      if (jj < w.nbk) total = total + readlane_f(mine, jj);
+    const float inv = inv_rms(total, (float)(1.0 / (double)a.P), a.eps);
+    add_products<MODE>(w.xr[mm], w.g, inv, readlane_f(w.wk, mm), w.acc);
+  }
+  w.poll = next_poll;
+  if constexpr (k + 1 < KMAX + kLag + 1) tp_step<MODE, KMAX, kAhead, k + 1>(a, w);
+}
+
+template <int MODE, bool WBF16, int KMAX, int kAhead>
+__global__ void __launch_bounds__(512) tp_mail_kernel(TpMailArgs a) {
+  TpWave<KMAX> w;
+  w.lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t = blockIdx.y;
+  w.nbk = (a.P + kBlockCols - 1) / kBlockCols;
+  w.j = blockIdx.x * a.wpb + wave;
+  if (w.j >= w.nbk) return;  // a spare wave of the last block (nothing below waits for it)
+  w.col = (w.j * kWave + w.lane) * kChunk;
+  w.has = w.col < a.P;
+  w.colc = w.has ? w.col : a.P - kChunk;  // lanes past the row read a valid chunk
+
+  // First loads: the route list (lane k < K: route k's row and weight) and
+  // the token's generation.  Absent routes have no bit in `present`.
+  w.e = -1;
+  w.wk = 0.0f;
+  if (w.lane < a.K) {
+    w.e = a.idx[(int64_t)t * a.K + w.lane];
+    w.wk = load_weight<WBF16>(a.w, (int64_t)t * a.K + w.lane);
+  }
+  unsigned g0 = 0;
+  if (w.lane == 0) g0 = __hip_atomic_load(a.gen + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  w.present = __ballot(w.lane < a.K && w.e >= 0 && (int64_t)w.e < a.num_rows);
+  unpack8(load16(a.gamma + w.colc), w.g);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) w.g[c] = w.g[c] + a.gain_center;
+  w.tag = (unsigned)__builtin_amdgcn_readfirstlane((int)g0) + 1u;
+  w.tslots = a.slots + (int64_t)t * KMAX * w.nbk;
+  w.limit = a.wait_ticks;
+  w.poll = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) w.acc[c] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k)
+    tp_issue(a, (w.present >> k) & 1ull, readlane_i(w.e, k), w.colc, w.q[k]);
+  tp_step<MODE, KMAX, kAhead, 0>(a, w);
+  if (w.has) store16(a.out + (int64_t)t * a.P + w.col, pack8_pz(w.acc));
+  if (w.lane == 0)
+    __hip_atomic_fetch_max(a.gen + t, w.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------ latent combine ---
 //
 // One block per token (latent_norm_body in norm_device.h).
@@ -487,7 +728,39 @@ hipError_t tp_norm_launch(const TpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Waves per block and routes in flight ahead of the one being added.
+constexpr int kTpWavesPerBlock = 7;
+constexpr int kTpAhead = 1;
+
+template <int MODE, bool WBF16, int KMAX>
+hipError_t tp_mail_launch(const TpMailArgs& p, int b, hipStream_t s) {
+  const int nbk = (p.P + kBlockCols - 1) / kBlockCols;
+  const int blocks = (nbk + p.wpb - 1) / p.wpb;
+  hipLaunchKernelGGL((tp_mail_kernel<MODE, WBF16, KMAX, kTpAhead>), dim3(blocks, b),
+                     dim3(kWave * p.wpb), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int MODE, bool WBF16>
+hipError_t tp_mail_dispatch_k(const TpMailArgs& p, int b, hipStream_t s) {
+  return p.K <= 16 ? tp_mail_launch<MODE, WBF16, 16>(p, b, s)
+                   : tp_mail_launch<MODE, WBF16, 32>(p, b, s);
+}
+
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t s) {
+  if (a.tp <= kTpOnePassMaxRanks) {
+    // one pass: a wave per 512 columns, blocks of kTpWavesPerBlock waves
+    const int nbk = (a.P + kBlockCols - 1) / kBlockCols;
+    const int wpb = nbk < kTpWavesPerBlock ? nbk : kTpWavesPerBlock;
+    TpMailArgs p{a.kpart, a.num_rows, a.idx, a.w, a.gamma, a.gain_center, a.eps, a.K, a.P, a.tp,
+                 a.out, a.gen, a.slots, wpb, a.wait_ticks};
+    switch ((a.wbn != 0 ? 2 : 0) + (a.w_bf16 != 0 ? 1 : 0)) {
+      case 0: return tp_mail_dispatch_k<kGainAfter, false>(p, a.b, s);
+      case 1: return tp_mail_dispatch_k<kGainAfter, true>(p, a.b, s);
+      case 2: return tp_mail_dispatch_k<kGainFirst, false>(p, a.b, s);
+      default: return tp_mail_dispatch_k<kGainFirst, true>(p, a.b, s);
+    }
+  }
   const int routes = a.b * a.K;
   const int nbk = (a.P + kBlockCols - 1) / kBlockCols;
   const int64_t waves = (int64_t)routes * nbk;

@@ -39,9 +39,15 @@ struct TpArgs {
   int wbn;
   int b, K, P, tp;
   uint16_t* out;          // [b][P]
+  // tp <= kTpOnePassMaxRanks: one pass, two blocks a token exchanging through
+  unsigned* gen;          // workspace [b]: each token's generation (zero at first use)
+  uint64_t* slots;        // workspace [b][K][ceil(P/512)]: tagged block totals
+  long long wait_ticks;   // the exchange's wait limit (100 MHz ticks; < 0: none)
+  // more ranks: two passes through
   uint16_t* xr;           // workspace [b][K][P]: rank-summed route rows
   float* block_total;     // workspace [b][K][ceil(P/512)]: their sum-of-squares block totals
 };
+constexpr int kTpOnePassMaxRanks = 8;  // the one-pass expert-TP kernel holds 8 ranks' loads
 hipError_t launch_tp_finalize(const TpArgs& a, hipStream_t stream);
 
 // Latent combine + RMSNorm: y[b][L] = bf16((bf16(sum_d lat[d]) * inv) * gamma).

@@ -135,10 +135,19 @@ int moetail_finalize(const uint16_t* rows, int64_t rows_per_rank,
  *                 [0, num_rows) marks an absent route (contributes nothing).
  *   route_w       [b][K] FP32 or BF16.   gamma [P] BF16.   out [b][P] BF16.
  *   workspace     at least moetail_workspace_bytes(MOETAIL_OP_TP_FINALIZE,
- *                 b, K, P, 0) bytes (the rank-summed route rows x_r,
- *                 [b][K][P] BF16, then their sum-of-squares totals per
- *                 512-column block, [b][K][ceil(P/512)] FP32), 256-byte
- *                 aligned.
+ *                 b, K, P, tp) bytes, 256-byte aligned, and ZERO BEFORE ITS
+ *                 FIRST USE (every call leaves it so).  With tp <= 8 the
+ *                 finalize is one pass: two blocks a token (the row's two
+ *                 halves) keep x_r on chip and meet once through the
+ *                 workspace's first words ([b][2] flags, then each half's
+ *                 sum-of-squares block totals [b][2][K][8] FP32); a wait
+ *                 for the other half is bounded (moetail_set_tp_wait_limit)
+ *                 and past it a block forms the other half's totals itself,
+ *                 so results never depend on the two running at once.  With
+ *                 more ranks (or tp = 0 in the size query) the workspace
+ *                 also holds the two-pass path's x_r rows [b][K][P] BF16
+ *                 and their 512-column block totals [b][K][ceil(P/512)] FP32.
+ *                 Calls that overlap must not share a workspace.
  *   Limits: 1 <= K <= 32, 1 <= tp <= 32, 8 <= P <= 8192, P % 8 == 0.
  */
 int moetail_tp_finalize(const uint16_t* kpartials, int64_t num_rows,
@@ -318,7 +327,7 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
 /*
  * Workspace bytes an operation needs (0 when none):
  *   MOETAIL_OP_FINALIZE:            0
- *   MOETAIL_OP_TP_FINALIZE:         dim0 = K, dim1 = P
+ *   MOETAIL_OP_TP_FINALIZE:         dim0 = K, dim1 = P, dim2 = tp (0: any tp)
  *   MOETAIL_OP_COMBINE_NORM_UPPROJ: dim0 = L, dim1 = N, dim2 = tp
  *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
  *   MOETAIL_OP_TAIL:                dim0 = L, dim1 = H, dim2 = I
@@ -346,6 +355,14 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);
  */
 int moetail_set_projection_tuning(int kind, int splits, int waves, int blocks,
                                   int tiles_per_unit, int prefetch, int passes);
+
+/*
+ * The one-pass expert-TP finalize's wait limit for the meeting of a token's
+ * two blocks, in ticks of the GPU's 100 MHz clock (default 2,000,000: 20 ms).
+ * A negative value skips the wait: every block forms its partner's totals
+ * itself (slower, the same bits).  For tests of that path; process-wide.
+ */
+void moetail_set_tp_wait_limit(int64_t ticks);
 
 /*
  * Plan searches and plan-cache hits so far in this process.  The projection

@@ -117,7 +117,11 @@ def test_tp_finalize_validation():
     assert _tp(P=7170) == mt.EUNSUPPORTED
     assert _tp(K=40) == mt.EUNSUPPORTED
     assert _tp(ws=None, wsb=0) == mt.EWORKSPACE
-    assert _tp(wsb=4 * 16 * 7168 * 2 - 2) == mt.EWORKSPACE
+    # tp = 8: the generations [4] and tagged block totals [4][16][14] (7424 B)
+    assert _tp(wsb=256 + 7168 - 1) == mt.EWORKSPACE
+    # tp = 12: the two-pass path's rows and totals as well
+    assert _tp(tp=12, wsb=256 + 7168) == mt.EWORKSPACE
+    assert _tp(tp=12, wsb=256 + 7168 + 4 * 16 * 7168 * 2 + 3584 - 1) == mt.EWORKSPACE
     assert _tp(ws=A + 128) == mt.EWORKSPACE
 
 
@@ -234,9 +238,17 @@ def test_workspace_query(b):
     sh = mt.workspace_bytes(mt.OP_SHARED_EXPERT, b, 7168, 6144)
     assert sh >= b * 6144 * 2 and sh % 256 == 0
     assert mt.workspace_bytes(mt.OP_FINALIZE, b, 3584) == 0
-    # the rank-summed rows [b][16][7168] BF16, then their 14 block totals a route in FP32
-    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168) == (
-        b * 16 * 7168 * 2 + (b * 16 * 14 * 4 + 255) // 256 * 256)
+    # the token generations [b] and the tagged block totals [b][16][14] (8 B
+    # each; 16 routes' slots for K <= 16, 32 above); for more than 8 ranks (or any tp, 0) also the rank-summed rows
+    # [b][16][7168] BF16 and their 14 block totals a route in FP32
+    def up256(n):
+        return (n + 255) // 256 * 256
+    sync = up256(b * 4) + up256(b * 16 * 14 * 8)
+    two_pass = b * 16 * 7168 * 2 + up256(b * 16 * 14 * 4)
+    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168) == sync + two_pass
+    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168, 8) == sync
+    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168, 9) == sync + two_pass
+    assert mt.workspace_bytes(mt.OP_TP_FINALIZE, b, 16, 7168, 33) == 0
     assert mt.workspace_bytes(99, b, 1, 1, 1) == 0
     assert mt.workspace_bytes(mt.OP_SHARED_EXPERT, 0, 7168, 6144) == 0
 

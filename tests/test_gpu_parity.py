@@ -235,7 +235,8 @@ def test_tp_full_scale(wbn, wkey):
 
 
 @pytest.mark.parametrize("b,K,P,tp", [(7, 5, 1032, 3), (3, 20, 520, 2), (2, 16, 8192, 1),
-                                      (5, 1, 8, 32), (4, 32, 3584, 4)])
+                                      (5, 1, 8, 32), (4, 32, 3584, 4), (3, 4, 512, 8),
+                                      (6, 16, 7168, 8), (3, 7, 2056, 12)])
 @pytest.mark.parametrize("wbn", [True, False])
 def test_tp_ragged_and_edges(b, K, P, tp, wbn):
     inp = workloads.tp_finalize(b + K, b=b, K=K, P=P, tp=tp, num_rows=b * K + 3)
@@ -249,6 +250,60 @@ def test_tp_ragged_and_edges(b, K, P, tp, wbn):
     got = run_tp(inp, wbn)
     finalize_bar(got, want, "tp out")
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("b,K,P,tp", [(16, 16, 7168, 8), (7, 5, 1032, 3), (4, 32, 3584, 4)])
+def test_tp_one_pass_when_the_halves_do_not_meet(b, K, P, tp):
+    """With no wait at all every block forms its partner half's block totals
+    itself: the same bits as the oracle (the path a block takes when its
+    partner does not come within the wait limit)."""
+    inp = workloads.tp_finalize(b + P, b=b, K=K, P=P, tp=tp, num_rows=b * K + 2)
+    idx = inp["idx"].copy()
+    idx[0, 0] = -1
+    inp["idx"] = idx
+    want = oracle.tp_finalize(inp["kpart"], idx, inp["w32"], inp["gamma"], 0.0, inp["eps"], False,
+                              nthreads=NT)
+    try:
+        mt.set_tp_wait_limit(-1)
+        got = run_tp(inp, False)
+    finally:
+        mt.set_tp_wait_limit()
+    assert np.array_equal(got, want)
+
+
+def test_tp_workspace_reused_and_graph_replay():
+    """One workspace serves many calls, eager and replayed from a graph, with
+    the same bits: every call raises each token's generation by one, so its
+    block-total slots are told apart from the last call's."""
+    inp = workloads.tp_finalize(5, b=32, K=16, P=7168, tp=8)
+    want = oracle.tp_finalize(inp["kpart"], inp["idx"], inp["w32"], inp["gamma"], 0.0, inp["eps"],
+                              False, nthreads=NT)
+    kp, idx, w, gamma = dev(inp["kpart"]), dev(inp["idx"]), dev(inp["w32"]), dev(inp["gamma"])
+    ws = mt.new_workspace(mt.OP_TP_FINALIZE, 32, 16, 7168, 8)
+    out = empty_bf16(32, 7168)
+
+    def call():
+        mt.moetail_tp_finalize(kp, idx, w, gamma, 0.0, inp["eps"], False, out, workspace=ws)
+
+    def generations():
+        torch.cuda.synchronize()
+        return ws[: 4 * 32].view(torch.int32).cpu().numpy().copy()
+
+    for i in range(3):
+        out.fill_(SENTINEL)
+        call()
+        assert np.array_equal(host(out), want)
+        assert np.all(generations() == i + 1)
+    g, st = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=st):
+        call()
+    for _ in range(3):
+        out.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), want)
+    assert np.all(generations() == 3 + 3)  # three eager calls, three replays
 
 
 def test_tp_no_norm_mode_is_refused_and_writes_nothing():

@@ -53,13 +53,13 @@ def graph_steps(steps: int) -> int:
 
 
 # HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
-# rocprofv3 --pmc passes over `bench.py --steps 8 --warmup 8 --no-cpu-baseline
-# --no-kernels --copy-calibration`: FETCH_SIZE and WRITE_SIZE per dispatch,
+# rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
+# WRITE_SIZE, per dispatch, the two decode steps' tail kernels averaged),
 # scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
 # out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
 # with this digest only.
-TRAFFIC = dict(source_digest="1501562b16dbe671", fetch_bytes=176014 * 2 * 1024,
-               write_bytes=33216 * 1024)
+TRAFFIC = dict(source_digest="85f1dc3e03bb2535", fetch_bytes=176206 * 2 * 1024,
+               write_bytes=33223 * 1024)
 
 
 def kernel_source_digest():
@@ -108,6 +108,11 @@ def main():
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
                     help="2: the finalize on a side stream beside the shared expert; "
                          "1: the three calls in order on one stream")
+    ap.add_argument("--counters", action="store_true",
+                    help="for rocprofv3 counter passes: a few eager calls of each workload (the "
+                         "decode step at b=64; finalize+combine b=64; expert TP b=128; combine+"
+                         "norm+up projection b=32; shared expert b=32 and 128), then two "
+                         "launches of the 256 MiB calibration kernel; no timing, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -196,6 +201,10 @@ def main():
         shared(d)
         main.wait_event(join)
         upproj(d)
+
+    if args.counters:
+        counter_workloads(sets, step, log, mt.W_TILED if args.weights == "tiled" else mt.W_ROWS)
+        return
 
     log("capturing the step graph")
     for d in sets:
@@ -436,6 +445,65 @@ def config_kernels(base, log, lay):
         add(f"shared_expert b={b}", us, 3 * H * I * 2 + 2 * b * H * 2,
             weight_roofline_us=round(3 * H * I * 2 / HBM_PEAK_GBPS / 1e3, 2))
     return res
+
+
+def counter_workloads(sets, step, log, lay, reps=2):
+    """Eager calls of every workload, reps each, for counter passes (each
+    dispatch is its own row in rocprofv3's output): the decode step (five
+    kernels), then each workload of the per-config table once more."""
+    import numpy as np
+    import torch
+
+    import expert_finalize_rmsnorm_amd as mt
+    import workloads
+    from tests.gpu_util import dev
+
+    base = sets[0]
+    for i in range(reps):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    log(f"counters: {reps} decode steps")
+    part = torch.empty((TP, B, P), dtype=torch.int16, device="cuda")
+    out = torch.empty((B, P), dtype=torch.int16, device="cuda")
+    for _ in range(reps):
+        mt.moetail_finalize(base["rows"], base["idx"], base["w"], base["gamma"], 1.0, 1e-6, True,
+                            partials=part, out=out)
+    g0 = torch.Generator("cpu").manual_seed(0)
+    w32, _ = workloads.route_weights(g0, 128, 16)
+    tgamma = workloads.normal_bf16(g0, (7168,), 1.0, 0.05)
+    idx = torch.from_numpy(np.random.default_rng(0).permutation(2048).astype(np.int32).reshape(
+        128, 16)).cuda()
+    gen = torch.Generator("cuda").manual_seed(1234)
+    kp = (torch.randn((8, 2048, 7168), device="cuda", generator=gen) * 0.5).to(
+        torch.bfloat16).view(torch.int16)
+    tout = torch.empty((128, 7168), dtype=torch.int16, device="cuda")
+    tws = mt.new_workspace(mt.OP_TP_FINALIZE, 128, 16, 7168, 8)
+    for _ in range(reps):
+        mt.moetail_tp_finalize(kp, idx, dev(w32), dev(tgamma), 0.0, 1e-6, False, tout,
+                               workspace=tws)
+    del kp
+    lat = torch.randn((TP, 32, P), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+    o = torch.empty((32, H), dtype=torch.int16, device="cuda")
+    ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, 32, P, H, TP)
+    for _ in range(reps):
+        mt.moetail_combine_norm_upproj(lat, base["lgamma"], 1e-6, base["w_up"], o, workspace=ws,
+                                       w_layout=lay)
+    for b in (32, 128):
+        x = torch.randn((b, H), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
+        rs = torch.empty((b, H), dtype=torch.int16, device="cuda")
+        ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
+        for _ in range(reps):
+            mt.moetail_shared_expert(x, base["wg"], base["wu"], base["wd"], rs, workspace=ws,
+                                     w_layout=lay)
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("counters: finalize+combine b=64, expert TP b=128, combine+norm+upproj b=32, shared "
+        "expert b=32 and b=128, calibration 2 x neg over 256 MiB in, 256 MiB out")
 
 
 def cpu_model():

@@ -159,9 +159,8 @@ TailLayout tail_layout(int b, int L, int H, int I) {
   l.part_bytes = round_up(g > du ? g : du, 256);
   return l;
 }
-bool tail_ok(const TailLayout& l) {
-  return l.gate_up.splits && l.down.splits && l.up.splits && l.group.waves;
-}
+// (Without a grouped plan the down and up projections run as two launches.)
+bool tail_ok(const TailLayout& l) { return l.gate_up.splits && l.down.splits && l.up.splits; }
 
 // Plans are searched once per (operation, sizes, CU count, overrides) and
 // kept: the entry points look theirs up instead of searching on every call

@@ -362,7 +362,7 @@ __device__ __forceinline__ void px_body_mp(const FxArgs& a, int block) {
     }
   };
 
-  constexpr int kStage = 16;
+  constexpr int kStage = NT >= 8 ? 4 : 16;  // (8 token blocks: the accumulators take 32 registers)
   constexpr int kThreads = kWave * kWaves;
   const int cpt = klen / 8;  // 16-byte pieces per token and pass
   const int pieces = 16 * NT * cpt;
@@ -698,7 +698,6 @@ constexpr Shape kShapes[] = {{1, 8, 7},  {1, 8, 8},  {1, 8, 14}, {1, 8, 16}, {2,
 ProjPlan make_mp_plan(int b, int rows, int K, const ProjTuning& t) {
   const int tok = 16 * token_blocks(b);
   ProjPlan p{};
-  if (tok > 64) return p;
   const int kmax = ((kLdsBytes / (2 * tok)) - 8) / 128 * 128;
   const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
   const int tiles = rows / 16;
@@ -719,8 +718,10 @@ ProjPlan make_mp_plan(int b, int rows, int K, const ProjTuning& t) {
       if (t.waves > 0 && w != t.waves) continue;
       const int per_wave = (tiles + bps * w - 1) / (bps * w);
       // units held a wave: 4 at most; with 12 waves (168 registers a wave)
-      // and 4 token blocks, one
-      if (per_wave > 4 || (w == 12 && tok == 64 && per_wave > 1)) continue;
+      // and 4 token blocks, one; with 8 token blocks (32 accumulator
+      // registers a unit), one
+      if (per_wave > 4 || (w == 12 && tok == 64 && per_wave > 1) || (tok == 128 && per_wave > 1))
+        continue;
       if (per_wave < best_units) {
         best_units = per_wave;
         p.splits = splits;
@@ -744,6 +745,25 @@ ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTunin
   if (t.passes >= 2) {
     const ProjPlan mp = make_mp_plan(b, rows, K, t);
     if (mp.splits) return mp;
+  }
+  if (t.passes == 0 && token_blocks(b) == 8) {
+    // At 8 token blocks a slice holds at most 512 of K, so one pass a split
+    // needs 13-14 splits, whose FP32 partials (6.3 MB a split for the 12288
+    // gate/up rows) cost more than the weights they save streaming; with
+    // one unit a wave held in registers across 2-4 LDS passes the gate/up
+    // takes 4 splits and the down projection 6.  The fewest splits over the
+    // pass counts that fit; the single-pass plan where none does.
+    ProjPlan best{};
+    for (int passes = 2; passes <= 4; ++passes) {
+      ProjTuning tp = t;
+      tp.passes = passes;
+      const ProjPlan mp = make_mp_plan(b, rows, K, tp);
+      if (mp.splits && (!best.splits || mp.splits < best.splits)) best = mp;
+    }
+    ProjTuning t1 = t;
+    t1.passes = 1;
+    const ProjPlan one = make_plan(b, rows, K, always_partials, t1);
+    return (best.splits && best.splits < one.splits) ? best : one;
   }
   if (t.passes == 0 && token_blocks(b) == 4) {
     // The plan's choice: at 4 token blocks the LDS holds at most 1152 of K a
@@ -875,7 +895,10 @@ hipError_t mp_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
     case 1: return mp_launch<1, W, U>(a, p, s);
     case 2: return mp_launch<2, W, U>(a, p, s);
     case 4: return mp_launch<4, W, U>(a, p, s);
-    default: return hipErrorInvalidValue;  // not planned (more than 4 token blocks)
+    default:
+      // 8 token blocks: one unit a wave (the planner's limit)
+      if constexpr (U == 1) return mp_launch<8, W, 1>(a, p, s);
+      return hipErrorInvalidValue;
   }
 }
 
@@ -893,6 +916,7 @@ hipError_t mp_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   if (!a.partials) return hipErrorInvalidValue;  // the multi-pass kernel always writes partials
   const int u = p.hold <= 1 ? 1 : p.hold <= 2 ? 2 : 4;
   if (p.waves == 12 && token_blocks(a.b) == 4 && u > 1) return hipErrorInvalidValue;  // not planned
+  if (token_blocks(a.b) == 8 && u > 1) return hipErrorInvalidValue;                    // not planned
   switch ((p.waves == 12 ? 3 : 0) + (u == 1 ? 0 : u == 2 ? 1 : 2)) {
     case 0: return mp_dispatch_nt<8, 1>(a, p, s);
     case 1: return mp_dispatch_nt<8, 2>(a, p, s);
@@ -954,13 +978,16 @@ hipError_t group_mp_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int 
 hipError_t group_mp_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g, int blocks0,
                              int blocks, size_t lds, hipStream_t s) {
   const int ntb = token_blocks(a0.b);
-  if (g.hold > 4 || (g.waves == 12 && ntb == 4 && g.hold > 1)) return hipErrorInvalidValue;
+  if (g.hold > 4 || (g.waves == 12 && ntb == 4 && g.hold > 1) || (ntb == 8 && g.hold > 1))
+    return hipErrorInvalidValue;
   if (g.waves == 8) {
     switch (ntb) {
       case 1: return group_mp_launch<1, 8, 4>(a0, a1, blocks0, blocks, lds, s);
       case 2: return group_mp_launch<2, 8, 4>(a0, a1, blocks0, blocks, lds, s);
       case 4: return group_mp_launch<4, 8, 4>(a0, a1, blocks0, blocks, lds, s);
-      default: return hipErrorInvalidValue;  // not planned
+      default:
+        if (g.hold > 1) return hipErrorInvalidValue;  // not planned
+        return group_mp_launch<8, 8, 1>(a0, a1, blocks0, blocks, lds, s);
     }
   }
   if (g.waves == 12) {
@@ -968,7 +995,9 @@ hipError_t group_mp_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan
       case 1: return group_mp_launch<1, 12, 4>(a0, a1, blocks0, blocks, lds, s);
       case 2: return group_mp_launch<2, 12, 4>(a0, a1, blocks0, blocks, lds, s);
       case 4: return group_mp_launch<4, 12, 1>(a0, a1, blocks0, blocks, lds, s);
-      default: return hipErrorInvalidValue;  // not planned
+      default:
+        if (g.hold > 1) return hipErrorInvalidValue;  // not planned
+        return group_mp_launch<8, 12, 1>(a0, a1, blocks0, blocks, lds, s);
     }
   }
   return hipErrorInvalidValue;
@@ -1028,7 +1057,6 @@ GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1
   const int cu = device_cu_count();
   const int tok = 16 * token_blocks(b);
   GroupPlan best{0, 0, 0, 0, 0};
-  if (tok > 64) return best;
   const long long n0 = (long long)(p0.passes > 1 ? p0.passes : 1) * (p0.k_per_split / kKStep);
   const long long n1 = (long long)(p1.passes > 1 ? p1.passes : 1) * (p1.k_per_split / kKStep);
   long long best_cost = -1;
@@ -1040,7 +1068,8 @@ GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1
       const int pw0 = ((rows0 / 16) + bps0 * w - 1) / (bps0 * w);
       const int pw1 = ((rows1 / 16) + bps1 * w - 1) / (bps1 * w);
       const int pw = pw0 > pw1 ? pw0 : pw1;
-      if (pw > 4 || (w == 12 && tok == 64 && pw > 1)) continue;  // registers: as the plan's
+      if (pw > 4 || (w == 12 && tok == 64 && pw > 1) || (tok == 128 && pw > 1))
+        continue;  // registers: as the plan's
       const long long c0 = pw0 * n0, c1 = pw1 * n1;
       const long long cost = c0 > c1 ? c0 : c1;
       const int blocks = bps0 * p0.splits + bps1 * p1.splits;
@@ -1111,7 +1140,14 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   const int blocks0 = g.bps0 * down.splits;
   const int blocks = blocks0 + g.bps1 * up.splits;
   const size_t lds = down.lds > up.lds ? down.lds : up.lds;
-  if (g.mp) {
+  if (!g.waves) {
+    // no grid holds both (8 token blocks, one unit a wave): two launches of
+    // the same plans, so the same sums
+    dn.blocks_per_slice = down.blocks_per_slice;
+    upa.blocks_per_slice = up.blocks_per_slice;
+    e = fx_dispatch(dn, down, s);
+    if (e == hipSuccess) e = fx_dispatch(upa, up, s);
+  } else if (g.mp) {
     dn.passes = down.passes > 1 ? down.passes : 1;
     upa.passes = up.passes > 1 ? up.passes : 1;
     e = group_mp_dispatch(dn, upa, g, blocks0, blocks, lds, s);

@@ -51,9 +51,11 @@ ProjPlan check_plan(int b, int rows, int K, bool always, const ProjTuning& t, co
   const int per_wave = ceil_div(rows / (16 * mr), p.blocks_per_slice * p.waves);
   if (p.passes > 1) {
     CHECK(K == p.splits * p.passes * p.k_per_split, CTX);
-    CHECK(tok <= 64 && mr == 1 && (p.waves == 8 || p.waves == 12), CTX);
+    CHECK(mr == 1 && (p.waves == 8 || p.waves == 12), CTX);
     CHECK(per_wave <= p.hold && p.hold <= 4, CTX);
     CHECK(!(p.waves == 12 && tok == 64 && p.hold > 1), CTX);
+    CHECK(!(tok == 128 && p.hold > 1), CTX);  // 8 token blocks: one unit a wave
+    CHECK(p.lds <= 160 * 1024, CTX);
   } else {
     CHECK((p.splits - 1) * p.k_per_split < K && K <= p.splits * p.k_per_split, CTX);
     if (p.hold) CHECK(mr == 1 && p.pf == 8 && p.waves <= 8 && tok <= 64, CTX);
@@ -82,9 +84,10 @@ void check_group(int b, int H, int I, int L, const ProjTuning& td, const ProjTun
   const int pw1 = ceil_div(H / 16, g.bps1 * g.waves);
   if (g.mp) {
     CHECK(dn.passes > 1 || up.passes > 1, CTX);
-    CHECK(tok <= 64 && (g.waves == 8 || g.waves == 12), CTX);
+    CHECK(g.waves == 8 || g.waves == 12, CTX);
     CHECK(pw0 <= g.hold && pw1 <= g.hold && g.hold <= 4, CTX);
     CHECK(!(g.waves == 12 && tok == 64 && g.hold > 1), CTX);
+    CHECK(!(tok == 128 && g.hold > 1), CTX);
     // (A single-pass side runs as one pass of its own slices, in units of
     // one tile whatever its plan's tiles per unit: each tile's chain keeps
     // its k order, so the sums are those of its own launch.)
@@ -121,10 +124,11 @@ int main() {
       check_plan(b, s.rows, s.K, s.always, dflt, "default");
       for (const ProjTuning& t : over) check_plan(b, s.rows, s.K, s.always, t, "override");
     }
-    // the tail's real shapes: a grouped plan must exist at every supported size
-    check_group(b, 7168, 6144, 3584, dflt, dflt, true, "tail");
-    check_group(b, 512, 320, 1024, dflt, dflt, true, "tail small");
-    check_group(b, 512, 128, 544, dflt, dflt, true, "tail ragged");
+    // the tail's real shapes: a grouped plan must exist at every size up to
+    // 64 tokens (above, the down and up projections may run as two launches)
+    check_group(b, 7168, 6144, 3584, dflt, dflt, b <= 64, "tail");
+    check_group(b, 512, 320, 1024, dflt, dflt, b <= 64, "tail small");
+    check_group(b, 512, 128, 544, dflt, dflt, b <= 64, "tail ragged");
     for (const ProjTuning& td : over)
       for (const ProjTuning& tu : over) check_group(b, 512, 320, 1024, td, tu, false, "tail override");
   }

@@ -69,6 +69,7 @@ struct ProjPlan {
   int blocks_per_slice;
   int hold;          // units a wave keeps in registers until its stream ends
   int passes;        // LDS slices of k_per_split per split (0 or 1: one; more: the multi-pass kernel)
+  int stream;        // 1: the streamed kernel (activations through an LDS chunk ring)
 };
 // Plan knobs: 0 = the library's choice.
 struct ProjTuning {
@@ -95,6 +96,7 @@ struct GroupPlan {
   int waves;
   int hold;
   int mp;  // both in the multi-pass kernel (either plan has passes > 1)
+  int stream;  // both in the streamed kernel (both plans streamed)
 };
 GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1);
 

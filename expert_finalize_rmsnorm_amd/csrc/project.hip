@@ -470,6 +470,220 @@ __device__ __forceinline__ void px_body_mp(const FxArgs& a, int block) {
             hold[j][nt];
 }
 
+// Streamed activations.  The block's K range is cut into chunks of
+// kStreamCols<NT> columns (32 KB of activations for any token count) and
+// wave kW of the block is a producer: it copies chunk after chunk of
+// X[16*NT tokens][chunk] into a ring of kRing LDS buffers with direct
+// global->LDS loads (no registers, and its loads never sit in a consumer's
+// memory queue), up to kRing chunks ahead of the slowest consumer.  Waves
+// 0 .. kW-1 are consumers: each streams the weights of its units -- a
+// kPF-deep register ring that runs across chunk and unit boundaries -- in
+// (chunk, unit, k step) order, every unit's FP32 sum held in registers over
+// the whole range.  Nothing makes a consumer stop for the activations
+// unless the producer has fallen behind: no pass boundary and no block
+// barrier after the first.  Each unit is one in-order MFMA chain over the
+// split's K range, so a split gives the same sums as in the other kernels.
+//
+// LDS: kRing chunk buffers, then the flags: [0] chunks filled, [1 + w]
+// chunks consumer w is done with.  Within a chunk, token row t holds its
+// 16-byte pieces in the order piece ^ (t % 16): the 16 tokens that one
+// operand read takes then sit in 16 different bank groups.
+constexpr int kRing = 4;
+constexpr int kStreamChunkBytes = 32 * 1024;
+constexpr int kStreamLds = kRing * kStreamChunkBytes + 256;
+constexpr int kStreamLoads = kStreamChunkBytes / 1024;  // 1 KB direct loads per chunk
+constexpr int kSpinLimit = 1 << 20;  // polls before a wait gives up (never reached in practice)
+template <int NT>
+constexpr int kStreamCols = kStreamChunkBytes / (2 * 16 * NT);
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// The LDS flags are read and written as relaxed workgroup-scope atomics:
+// plain LDS reads and writes, which one wave's LDS operations keep in
+// order, without the waits for every memory operation in flight that a
+// volatile access or an acquire would add (they would drain the weight
+// ring).
+__device__ __forceinline__ int flag_get(const int* f) {
+  return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_set(int* f, int v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Waits until at least `need` chunks are filled (consumers) -- a bounded
+// poll of the LDS flag; the memory clobber keeps the chunk's reads after it.
+__device__ __forceinline__ void wait_filled(int* flags, int need) {
+  for (int it = 0; it < kSpinLimit && flag_get(flags) < need; ++it) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
+}
+
+template <int NT, int kW>
+__device__ __forceinline__ void stream_producer(const FxArgs& a, uint16_t* xs, int* flags,
+                                                int kb0, int nchunks) {
+  constexpr int kC = kStreamCols<NT>;
+  constexpr int kChunkElems = kStreamChunkBytes / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int x = 0; x < nchunks; ++x) {
+    if (x >= kRing) {
+      // buffer x % kRing is free once every consumer is done with chunk x - kRing
+      const int need = x - kRing + 1;
+      for (int it = 0; it < kSpinLimit; ++it) {
+        const int v = lane < kW ? flag_get(flags + 1 + lane) : need;
+        if (__ballot(v < need) == 0) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+    }
+    uint16_t* buf = xs + (x % kRing) * kChunkElems;
+    const int col0 = kb0 + x * kC;
+#pragma unroll
+    for (int j = 0; j < kStreamLoads; ++j) {
+      const int e = j * 512 + lane * 8;  // element of the chunk this lane fills
+      const int t = e / kC;
+      const int s = ((e - t * kC) >> 3) ^ (t & 15);
+      const int col = min(col0 + 8 * s, a.K - 8);  // past the range: a valid piece, never read
+      const uint16_t* g = a.X + (int64_t)min(t, a.b - 1) * a.K + col;
+      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
+    }
+    // the chunk has landed in LDS, then it is published (an LDS write
+    // after direct loads waits for them in any case)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) flag_set(flags, x + 1);
+  }
+}
+
+template <int NT, int kW, int kPF, int kMaxU>
+__device__ __forceinline__ void px_body_stream(const FxArgs& a, int block) {
+  constexpr int kC = kStreamCols<NT>;
+  constexpr int kChunkElems = kStreamChunkBytes / 2;
+  extern __shared__ uint16_t xs[];
+  int* flags = reinterpret_cast<int*>(xs + kRing * kChunkElems);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lrow = lane & 15;
+  const int kq = lane >> 4;
+  const int K = a.K;
+  const int split = block / a.blocks_per_slice;
+  const int kb0 = split * a.k_per_split;
+  const int klen = min(a.k_per_split, K - kb0);
+  const int nchunks = (klen + kC - 1) / kC;
+  if (threadIdx.x < 1 + kW) flag_set(flags + threadIdx.x, 0);
+  __syncthreads();
+  if (wave == kW) {
+    stream_producer<NT, kW>(a, xs, flags, kb0, nchunks);
+    return;
+  }
+
+  const int stride = a.blocks_per_slice * kW;
+  const int u = (block - split * a.blocks_per_slice) * kW + wave;
+  const int nunits = a.N / 16;
+  const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // <= kMaxU
+  if (my_units == 0) {
+    if (lane == 0) flag_set(flags + 1 + wave, nchunks);
+    return;
+  }
+  const int total = my_units * (klen / kKStep);
+  auto chunk_steps = [&](int c) { return min(kC, klen - c * kC) / kKStep; };
+
+  const int64_t lane_off = a.tiled ? 8 * lane : (int64_t)lrow * K + 8 * kq;
+  const int k_mul = a.tiled ? 16 : 1;
+  const int step_stride = a.tiled ? 512 : kKStep;
+  auto unit_ptr = [&](int i, int c) {
+    const int row0 = (u + i * stride) * 16;
+    const uint16_t* base = row0 < a.n0 ? a.A0 + (int64_t)row0 * K
+                                       : a.A1 + (int64_t)(row0 - a.n0) * K;
+    return base + lane_off + (int64_t)(kb0 + c * kC) * k_mul;
+  };
+  // Load cursor over (chunk, unit, step), in the order of the MFMAs; past
+  // the wave's last step it stays on it (every ring slot refills).
+  int l_step = 0, l_i = 0, l_chunk = 0, l_left = total, l_ns = chunk_steps(0);
+  const uint16_t* l_ptr = unit_ptr(0, 0);
+  auto next_load = [&](uint4& q) {
+    q = load16_stream(l_ptr + l_step * step_stride);
+    if (l_left > 1) {
+      --l_left;
+      if (++l_step == l_ns) {
+        l_step = 0;
+        if (++l_i == my_units) {
+          l_i = 0;
+          ++l_chunk;
+          l_ns = chunk_steps(l_chunk);
+        }
+        l_ptr = unit_ptr(l_i, l_chunk);
+      }
+    }
+  };
+  uint4 ra[kPF];
+#pragma unroll
+  for (int i = 0; i < kPF; ++i) next_load(ra[i]);
+
+  f32x4_t acc[NT];
+  f32x4_t hold[kMaxU][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < kMaxU; ++j)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) hold[j][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // operand reads: token row 16 nt + lrow, piece (4 step + kq) ^ lrow
+  int c_step = 0, c_i = 0, c_chunk = 0, c_ns = chunk_steps(0);
+  const uint16_t* xrow = xs + lrow * kC;
+  wait_filled(flags, 1);
+
+  for (int q0 = 0; q0 < total; q0 += kPF) {
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) {
+      if (q0 + i < total) {
+        const uint16_t* xp = xrow + (((4 * c_step + kq) ^ lrow) << 3);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint4 bq = *reinterpret_cast<const uint4*>(xp + 16 * nt * kC);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ra[i]), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0,
+              0, 0);
+        }
+        if (++c_step == c_ns) {
+          // park this unit's sum, take up the next one's (register moves:
+          // the slot index is wave-uniform)
+          c_step = 0;
+          const int next_i = c_i + 1 == my_units ? 0 : c_i + 1;
+#pragma unroll
+          for (int j = 0; j < kMaxU; ++j)
+            if (j == c_i)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) hold[j][nt] = acc[nt];
+#pragma unroll
+          for (int j = 0; j < kMaxU; ++j)
+            if (j == next_i)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) acc[nt] = hold[j][nt];
+          c_i = next_i;
+          if (c_i == 0) {
+            // this wave is done with the chunk: its buffer may be refilled
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            ++c_chunk;
+            if (lane == 0) flag_set(flags + 1 + wave, c_chunk);
+            if (c_chunk < nchunks) {
+              c_ns = chunk_steps(c_chunk);
+              xrow = xs + (c_chunk % kRing) * kChunkElems + lrow * kC;
+              wait_filled(flags, c_chunk + 1);
+            }
+          }
+        }
+      }
+      next_load(ra[i]);
+    }
+  }
+  const int ntiles = a.N / 16;
+#pragma unroll
+  for (int j = 0; j < kMaxU; ++j)
+    if (j < my_units)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        a.partials[(((int64_t)split * ntiles + u + j * stride) * NT + nt) * kWave + lane] =
+            hold[j][nt];
+}
+
 // Blocks reach the 8 XCDs in turn (block g on XCD g % 8), and each XCD has
 // its own L2.  The position of block g among the blocks [s, s + m) sorted
 // by (XCD, index): consecutive positions share an XCD, so the blocks of one
@@ -522,6 +736,22 @@ __global__ void __launch_bounds__(kWave * kWaves) px_group_mp_kernel(FxArgs a0, 
     px_body_mp<NT, kWaves, kMaxU>(a0, xcd_position(blockIdx.x, 0, blocks0));
   else
     px_body_mp<NT, kWaves, kMaxU>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
+}
+
+template <int NT, int kW, int kPF, int kMaxU>
+__global__ void __launch_bounds__(kWave * (kW + 1)) px_stream_kernel(FxArgs a) {
+  px_body_stream<NT, kW, kPF, kMaxU>(a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
+}
+
+// Two independent projections in one streamed grid (the fused tail's down
+// and up projections).
+template <int NT, int kW, int kPF, int kMaxU>
+__global__ void __launch_bounds__(kWave * (kW + 1)) px_group_stream_kernel(FxArgs a0, FxArgs a1,
+                                                                         int blocks0) {
+  if ((int)blockIdx.x < blocks0)
+    px_body_stream<NT, kW, kPF, kMaxU>(a0, xcd_position(blockIdx.x, 0, blocks0));
+  else
+    px_body_stream<NT, kW, kPF, kMaxU>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
 }
 
 // Slice partials added in slice order, then the epilogue: one thread per
@@ -741,7 +971,64 @@ ProjPlan make_mp_plan(int b, int rows, int K, const ProjTuning& t) {
   return p;
 }
 
+// The streamed kernel's shapes: (consumer waves, prefetch depth, units held
+// a wave).  One block of kW + 1 waves per CU.
+struct StreamShape {
+  int waves, pf, units;
+};
+constexpr StreamShape kStreamShapes[] = {{6, 16, 1}, {7, 16, 1}};
+
+// The streamed plan: `splits` K ranges (multiples of the k step; the last
+// may be shorter), the CUs shared evenly between them, every wave of a
+// split at most one unit.  The modelled cost: the longest wave stream times
+// the waves of all CUs (the time the weights take, idle waves included),
+// the FP32 partials written and re-read, and the activations the blocks
+// read from L2 (at a fifth of the weight cost).
+ProjPlan make_stream_plan(int b, int rows, int K, const ProjTuning& t) {
+  const int tok = 16 * token_blocks(b);
+  const int blocks = t.target_blocks > 0 ? t.target_blocks : device_cu_count();
+  const int tiles = rows / 16;
+  double best = 1e300;
+  ProjPlan p{};
+  for (int splits = 1; splits <= 32; ++splits) {
+    if (t.splits > 0 && splits != t.splits) continue;
+    const int kr = round_up_i((K + splits - 1) / splits, kKStep);
+    if ((K + kr - 1) / kr != splits) continue;
+    const int bps = blocks / splits;
+    if (bps < 1) continue;
+    for (const StreamShape& sh : kStreamShapes) {
+      if (t.waves > 0 && sh.waves != t.waves) continue;
+      if (t.pf > 0 && sh.pf != t.pf) continue;
+      const int per_wave = (tiles + bps * sh.waves - 1) / (bps * sh.waves);
+      if (per_wave > sh.units) continue;
+      const double cost = (double)blocks * sh.waves * per_wave * 16.0 * kr * 2.0 +
+                          (double)splits * tok * rows * 8.0 + 0.2 * blocks * tok * kr * 2.0;
+      if (cost < best * 0.999) {
+        best = cost;
+        p = ProjPlan{};
+        p.splits = splits;
+        p.k_per_split = kr;
+        p.pitch = 0;
+        p.lds = kStreamLds;
+        p.waves = sh.waves;
+        p.mr = 1;
+        p.pf = sh.pf;
+        p.blocks_per_slice = bps;
+        p.hold = per_wave;
+        p.passes = 1;
+        p.stream = 1;
+      }
+    }
+  }
+  return p;
+}
+
 ProjPlan make_plan(int b, int rows, int K, bool always_partials, const ProjTuning& t) {
+  if (t.passes == 0 && t.mr == 0) {
+    // the library's choice: the streamed kernel where a shape fits
+    const ProjPlan sp = make_stream_plan(b, rows, K, t);
+    if (sp.splits) return sp;
+  }
   if (t.passes >= 2) {
     const ProjPlan mp = make_mp_plan(b, rows, K, t);
     if (mp.splits) return mp;
@@ -927,7 +1214,38 @@ hipError_t mp_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
   }
 }
 
+template <int NT, int W, int PF, int U>
+hipError_t stream_launch(const FxArgs& a0, const ProjPlan& p, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_stream_kernel<NT, W, PF, U>), lds_set);
+  if (e != hipSuccess) return e;
+  FxArgs a = a0;
+  a.passes = 1;
+  hipLaunchKernelGGL((px_stream_kernel<NT, W, PF, U>), dim3(p.splits * p.blocks_per_slice),
+                     dim3(kWave * (W + 1)), kStreamLds, s, a);
+  return hipGetLastError();
+}
+
+template <int W, int PF, int U>
+hipError_t stream_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  switch (token_blocks(a.b)) {
+    case 1: return stream_launch<1, W, PF, U>(a, p, s);
+    case 2: return stream_launch<2, W, PF, U>(a, p, s);
+    case 4: return stream_launch<4, W, PF, U>(a, p, s);
+    default: return stream_launch<8, W, PF, U>(a, p, s);
+  }
+}
+
+hipError_t stream_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (!a.partials || p.hold != 1 || p.pf != 16) return hipErrorInvalidValue;  // not planned
+  if (p.waves == 6) return stream_dispatch_nt<6, 16, 1>(a, p, s);
+  if (p.waves == 7) return stream_dispatch_nt<7, 16, 1>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t fx_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (p.stream) return stream_dispatch(a, p, s);
   if (p.passes > 1) return mp_dispatch(a, p, s);
   if (p.hold && a.partials) {
     if (p.mr != 1 || p.pf != 8 || p.waves > 8 || token_blocks(a.b) > 4) return hipErrorInvalidValue;
@@ -1003,6 +1321,30 @@ hipError_t group_mp_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan
   return hipErrorInvalidValue;
 }
 
+template <int NT, int W, int PF, int U>
+hipError_t group_stream_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
+                               hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = allow_full_lds(
+      reinterpret_cast<const void*>(px_group_stream_kernel<NT, W, PF, U>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((px_group_stream_kernel<NT, W, PF, U>), dim3(blocks), dim3(kWave * (W + 1)),
+                     kStreamLds, s, a0, a1, blocks0);
+  return hipGetLastError();
+}
+
+// 7 consumer waves holding up to 2 units each.
+hipError_t group_stream_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g,
+                                 int blocks0, int blocks, hipStream_t s) {
+  if (g.waves != 7 || g.hold > 2) return hipErrorInvalidValue;  // not planned
+  switch (token_blocks(a0.b)) {
+    case 1: return group_stream_launch<1, 7, 16, 2>(a0, a1, blocks0, blocks, s);
+    case 2: return group_stream_launch<2, 7, 16, 2>(a0, a1, blocks0, blocks, s);
+    case 4: return group_stream_launch<4, 7, 16, 2>(a0, a1, blocks0, blocks, s);
+    default: return group_stream_launch<8, 7, 16, 2>(a0, a1, blocks0, blocks, s);
+  }
+}
+
 template <int W, int H>
 hipError_t group_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
                              size_t lds, hipStream_t s) {
@@ -1043,7 +1385,7 @@ ProjPlan plan_projection(int b, int rows, int K, bool always_partials, const Pro
 
 size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
   const size_t tok = 16 * (size_t)token_blocks(b);  // padded tokens are stored too
-  return (p.splits > 1 || p.passes > 1 || always) ? sizeof(float) * (size_t)p.splits * tok * n_out
+  return (p.splits > 1 || p.passes > 1 || p.stream || always) ? sizeof(float) * (size_t)p.splits * tok * n_out
                                                    : 0;
 }
 
@@ -1056,7 +1398,7 @@ size_t proj_partial_bytes(const ProjPlan& p, int b, int n_out, bool always) {
 GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
   const int cu = device_cu_count();
   const int tok = 16 * token_blocks(b);
-  GroupPlan best{0, 0, 0, 0, 0};
+  GroupPlan best{0, 0, 0, 0, 0, 0};
   const long long n0 = (long long)(p0.passes > 1 ? p0.passes : 1) * (p0.k_per_split / kKStep);
   const long long n1 = (long long)(p1.passes > 1 ? p1.passes : 1) * (p1.k_per_split / kKStep);
   long long best_cost = -1;
@@ -1076,18 +1418,33 @@ GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && blocks > best_blocks)) {
         best_cost = cost;
         best_blocks = blocks;
-        best = GroupPlan{bps0, bps1, w, pw, 1};
+        best = GroupPlan{bps0, bps1, w, pw, 1, 0};
       }
     }
   }
   return best;
 }
 
+// Both streamed: each keeps its K ranges; blocks per split the fewest that
+// give every wave at most 2 units (7 consumer waves), both grids on the CUs.
+GroupPlan plan_group_stream(const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
+  const int cu = device_cu_count();
+  constexpr int kW = 7, kU = 2;
+  const int bps0 = (rows0 / 16 + kW * kU - 1) / (kW * kU);
+  const int bps1 = (rows1 / 16 + kW * kU - 1) / (kW * kU);
+  if (bps0 * p0.splits + bps1 * p1.splits > cu) return GroupPlan{};
+  const int pw0 = (rows0 / 16 + bps0 * kW - 1) / (bps0 * kW);
+  const int pw1 = (rows1 / 16 + bps1 * kW - 1) / (bps1 * kW);
+  return GroupPlan{bps0, bps1, kW, pw0 > pw1 ? pw0 : pw1, 0, 1};
+}
+
 GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
+  if (p0.stream || p1.stream)
+    return (p0.stream && p1.stream) ? plan_group_stream(p0, rows0, p1, rows1) : GroupPlan{};
   if (p0.passes > 1 || p1.passes > 1) return plan_group_mp(b, p0, rows0, p1, rows1);
   const int cu = device_cu_count();
   const int tok = 16 * token_blocks(b);
-  GroupPlan best{0, 0, 0, 0, 0};
+  GroupPlan best{0, 0, 0, 0, 0, 0};
   long long best_cost = -1;
   int best_blocks = 0;
   for (int w = 7; w <= 8; ++w) {
@@ -1103,7 +1460,7 @@ GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, i
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && blocks > best_blocks)) {
         best_cost = cost;
         best_blocks = blocks;
-        best = GroupPlan{bps0, bps1, w, (tok <= 64 && pw0 <= 4 && pw1 <= 4) ? 4 : 0, 0};
+        best = GroupPlan{bps0, bps1, w, (tok <= 64 && pw0 <= 4 && pw1 <= 4) ? 4 : 0, 0, 0};
       }
     }
   }
@@ -1140,7 +1497,9 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   const int blocks0 = g.bps0 * down.splits;
   const int blocks = blocks0 + g.bps1 * up.splits;
   const size_t lds = down.lds > up.lds ? down.lds : up.lds;
-  if (!g.waves) {
+  if (g.stream) {
+    e = group_stream_dispatch(dn, upa, g, blocks0, blocks, s);
+  } else if (!g.waves) {
     // no grid holds both (8 token blocks, one unit a wave): two launches of
     // the same plans, so the same sums
     dn.blocks_per_slice = down.blocks_per_slice;
@@ -1178,7 +1537,7 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* pa
 hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint16_t* X, int b,
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
-  const bool split = plan.splits > 1 || plan.passes > 1;
+  const bool split = plan.splits > 1 || plan.passes > 1 || plan.stream;  // (streamed: always partials)
   f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
            split ? part : nullptr, rs, out, tiled};

@@ -42,6 +42,18 @@ ProjPlan check_plan(int b, int rows, int K, bool always, const ProjTuning& t, co
 #define CTX "%s b=%d rows=%d K=%d splits=%d kps=%d passes=%d waves=%d bps=%d hold=%d", what, b, \
             rows, K, p.splits, p.k_per_split, p.passes, p.waves, p.blocks_per_slice, p.hold
   CHECK(p.k_per_split > 0 && p.k_per_split % 32 == 0, CTX);
+  if (p.stream) {
+    // the streamed kernel: activations through the LDS chunk ring (fixed
+    // LDS), K ranges that cover K, 6 or 7 consumer waves with a 16-deep
+    // ring, one unit a wave
+    CHECK(p.lds == 4 * 32 * 1024 + 256, CTX);
+    CHECK((p.splits - 1) * p.k_per_split < K && K <= p.splits * p.k_per_split, CTX);
+    CHECK(p.blocks_per_slice >= 1 && p.splits * p.blocks_per_slice <= target, CTX);
+    CHECK((p.waves == 6 || p.waves == 7) && p.pf == 16 && p.mr == 1 && p.hold == 1, CTX);
+    CHECK(ceil_div(rows / 16, p.blocks_per_slice * p.waves) <= 1, CTX);
+    CHECK(rows % 16 == 0 && K % 8 == 0, CTX);
+    return p;
+  }
   CHECK(p.pitch >= p.k_per_split, CTX);
   CHECK(p.lds == (size_t)tok * p.pitch * 2 && p.lds <= 160 * 1024, CTX);
   CHECK(p.blocks_per_slice >= 1, CTX);
@@ -82,7 +94,11 @@ void check_group(int b, int H, int I, int L, const ProjTuning& td, const ProjTun
   CHECK(g.bps0 * dn.splits + g.bps1 * up.splits <= device_cu_count(), CTX);
   const int pw0 = ceil_div(H / 16, g.bps0 * g.waves);
   const int pw1 = ceil_div(H / 16, g.bps1 * g.waves);
-  if (g.mp) {
+  if (g.stream) {
+    // both streamed, 7 consumer waves holding up to 2 units
+    CHECK(dn.stream && up.stream && g.waves == 7, CTX);
+    CHECK(pw0 <= g.hold && pw1 <= g.hold && g.hold <= 2, CTX);
+  } else if (g.mp) {
     CHECK(dn.passes > 1 || up.passes > 1, CTX);
     CHECK(g.waves == 8 || g.waves == 12, CTX);
     CHECK(pw0 <= g.hold && pw1 <= g.hold && g.hold <= 4, CTX);
@@ -126,7 +142,7 @@ int main() {
     }
     // the tail's real shapes: a grouped plan must exist at every size up to
     // 64 tokens (above, the down and up projections may run as two launches)
-    check_group(b, 7168, 6144, 3584, dflt, dflt, b <= 64, "tail");
+    check_group(b, 7168, 6144, 3584, dflt, dflt, true, "tail");
     check_group(b, 512, 320, 1024, dflt, dflt, b <= 64, "tail small");
     check_group(b, 512, 128, 544, dflt, dflt, b <= 64, "tail ragged");
     for (const ProjTuning& td : over)

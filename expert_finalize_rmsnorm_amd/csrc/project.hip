@@ -517,12 +517,68 @@ __device__ __forceinline__ void wait_filled(int* flags, int need) {
   asm volatile("" ::: "memory");
 }
 
+// One projection's share of a streamed block: its K range (split) and the
+// units of it that this wave holds.  With two phases a block runs the
+// first projection's chunks, then the second's (the fused tail's down and
+// up projections: every wave one unit of each, equal work everywhere).
+struct StreamPhase {
+  const uint16_t* A0;
+  const uint16_t* A1;
+  const uint16_t* X;
+  f32x4_t* partials;
+  int n0, N, K, b, tiled, split;
+  int kb0, klen, nchunks, first_chunk;
+  int u, stride, units;  // this wave's first unit, unit stride, units held
+};
+
 template <int NT, int kW>
-__device__ __forceinline__ void stream_producer(const FxArgs& a, uint16_t* xs, int* flags,
-                                                int kb0, int nchunks) {
+__device__ __forceinline__ StreamPhase stream_phase(const FxArgs& a, int block, int first_chunk) {
+  constexpr int kC = kStreamCols<NT>;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  StreamPhase ph;
+  const int split = block / a.blocks_per_slice;
+  ph.A0 = a.A0;
+  ph.A1 = a.A1;
+  ph.X = a.X;
+  ph.partials = a.partials;
+  ph.n0 = a.n0;
+  ph.N = a.N;
+  ph.K = a.K;
+  ph.b = a.b;
+  ph.tiled = a.tiled;
+  ph.split = split;
+  ph.kb0 = split * a.k_per_split;
+  ph.klen = ph.kb0 < a.K ? min(a.k_per_split, a.K - ph.kb0) : 0;  // 0: no split here
+  ph.nchunks = (ph.klen + kC - 1) / kC;
+  ph.first_chunk = first_chunk;
+  ph.stride = a.blocks_per_slice * kW;
+  ph.u = (block - split * a.blocks_per_slice) * kW + wave;
+  const int nunits = a.N / 16;
+  ph.units = (ph.klen > 0 && ph.u < nunits) ? (nunits - ph.u + ph.stride - 1) / ph.stride : 0;
+  return ph;
+}
+
+// Phase-dependent values are chosen between plain local scalars (q0_f,
+// q1_f) by these macros, with no helper function or closure in between: a
+// helper that picks one of two fields in memory is simplified, before it
+// is inlined, into one load from a selected address, and the structure
+// behind it can then never live in registers (it goes to scratch memory).
+#define STREAM_FIELD(p, f) ((kPhases > 1 && (p) != 0) ? q1_##f : q0_##f)
+#define STREAM_LOCALS(f)           \
+  const auto q0_##f = ph0.f;       \
+  const auto q1_##f = ph1.f;
+
+template <int NT, int kW, int kPhases>
+__device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const StreamPhase& ph1,
+                                                uint16_t* xs, int* flags, int nchunks) {
   constexpr int kC = kStreamCols<NT>;
   constexpr int kChunkElems = kStreamChunkBytes / 2;
   const int lane = threadIdx.x & (kWave - 1);
+  const int b = ph0.b;
+  STREAM_LOCALS(X)
+  STREAM_LOCALS(K)
+  STREAM_LOCALS(kb0)
+  STREAM_LOCALS(first_chunk)
   for (int x = 0; x < nchunks; ++x) {
     if (x >= kRing) {
       // buffer x % kRing is free once every consumer is done with chunk x - kRing
@@ -534,15 +590,18 @@ __device__ __forceinline__ void stream_producer(const FxArgs& a, uint16_t* xs, i
       }
       asm volatile("" ::: "memory");
     }
+    const int p = (kPhases > 1 && x >= q1_first_chunk) ? 1 : 0;
+    const uint16_t* X = STREAM_FIELD(p, X);
+    const int K = STREAM_FIELD(p, K);
+    const int col0 = STREAM_FIELD(p, kb0) + (x - STREAM_FIELD(p, first_chunk)) * kC;
     uint16_t* buf = xs + (x % kRing) * kChunkElems;
-    const int col0 = kb0 + x * kC;
 #pragma unroll
     for (int j = 0; j < kStreamLoads; ++j) {
       const int e = j * 512 + lane * 8;  // element of the chunk this lane fills
       const int t = e / kC;
       const int s = ((e - t * kC) >> 3) ^ (t & 15);
-      const int col = min(col0 + 8 * s, a.K - 8);  // past the range: a valid piece, never read
-      const uint16_t* g = a.X + (int64_t)min(t, a.b - 1) * a.K + col;
+      const int col = min(col0 + 8 * s, K - 8);  // past the range: a valid piece, never read
+      const uint16_t* g = X + (int64_t)min(t, b - 1) * K + col;
       __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
     }
     // the chunk has landed in LDS, then it is published (an LDS write
@@ -552,8 +611,11 @@ __device__ __forceinline__ void stream_producer(const FxArgs& a, uint16_t* xs, i
   }
 }
 
-template <int NT, int kW, int kPF, int kMaxU>
-__device__ __forceinline__ void px_body_stream(const FxArgs& a, int block) {
+// kPhases (1 or 2) projections in one streamed block: a0's chunks, then
+// a1's (a1 unused with one phase); block: the block's position in both
+// grids.
+template <int NT, int kW, int kPF, int kMaxU, int kPhases>
+__device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a1, int block) {
   constexpr int kC = kStreamCols<NT>;
   constexpr int kChunkElems = kStreamChunkBytes / 2;
   extern __shared__ uint16_t xs[];
@@ -562,61 +624,92 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a, int block) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15;
   const int kq = lane >> 4;
-  const int K = a.K;
-  const int split = block / a.blocks_per_slice;
-  const int kb0 = split * a.k_per_split;
-  const int klen = min(a.k_per_split, K - kb0);
-  const int nchunks = (klen + kC - 1) / kC;
+  const StreamPhase ph0 = stream_phase<NT, kW>(a0, block, 0);
+  const StreamPhase ph1 = stream_phase<NT, kW>(kPhases > 1 ? a1 : a0, block, ph0.nchunks);
+  const int nchunks = ph0.nchunks + (kPhases > 1 ? ph1.nchunks : 0);
   if (threadIdx.x < 1 + kW) flag_set(flags + threadIdx.x, 0);
   __syncthreads();
   if (wave == kW) {
-    stream_producer<NT, kW>(a, xs, flags, kb0, nchunks);
+    stream_producer<NT, kW, kPhases>(ph0, ph1, xs, flags, nchunks);
     return;
   }
+  STREAM_LOCALS(A0)
+  STREAM_LOCALS(A1)
+  STREAM_LOCALS(n0)
+  STREAM_LOCALS(K)
+  STREAM_LOCALS(kb0)
+  STREAM_LOCALS(klen)
+  STREAM_LOCALS(nchunks)
+  STREAM_LOCALS(first_chunk)
+  STREAM_LOCALS(u)
+  STREAM_LOCALS(stride)
+  STREAM_LOCALS(units)
+  const int tiled = ph0.tiled;  // (every phase has the same layout)
 
-  const int stride = a.blocks_per_slice * kW;
-  const int u = (block - split * a.blocks_per_slice) * kW + wave;
-  const int nunits = a.N / 16;
-  const int my_units = u < nunits ? (nunits - u + stride - 1) / stride : 0;  // <= kMaxU
-  if (my_units == 0) {
+// chunk c's phase; its k steps for each of that phase's units; that
+// phase's units held by this wave; the first chunk from c on in which this
+// wave has units (nchunks: none); the hold slot of the phase's first unit
+#define PHASE_OF(c) ((kPhases > 1 && (c) >= q1_first_chunk) ? 1 : 0)
+#define CHUNK_STEPS(c) \
+  (min(kC, STREAM_FIELD(PHASE_OF(c), klen) - ((c) - STREAM_FIELD(PHASE_OF(c), first_chunk)) * kC) / kKStep)
+#define UNITS_OF(c) STREAM_FIELD(PHASE_OF(c), units)
+#define SKIP0(c) ((q0_units == 0 && (c) < q0_nchunks) ? q0_nchunks : (c))
+#define WORK_CHUNK(c) \
+  ((kPhases > 1 && q1_units == 0 && SKIP0(c) >= q1_first_chunk) ? nchunks : SKIP0(c))
+#define SLOT_BASE(c) ((kPhases > 1 && PHASE_OF(c) > 0) ? q0_units : 0)
+
+  const int total =
+      q0_units * (q0_klen / kKStep) + (kPhases > 1 ? q1_units * (q1_klen / kKStep) : 0);
+  if (total == 0) {
     if (lane == 0) flag_set(flags + 1 + wave, nchunks);
     return;
   }
-  const int total = my_units * (klen / kKStep);
-  auto chunk_steps = [&](int c) { return min(kC, klen - c * kC) / kKStep; };
+  const int64_t lane_off0 = tiled ? 8 * lane : (int64_t)lrow * q0_K + 8 * kq;
+  const int64_t lane_off1 = tiled ? 8 * lane : (int64_t)lrow * q1_K + 8 * kq;
+  const int k_mul = tiled ? 16 : 1;
+  const int step_stride = tiled ? 512 : kKStep;
+  // where unit i of chunk c starts (the chunk's first k step)
+#define UNIT_PTR(c, i, out)                                                                   \
+  do {                                                                                        \
+    const int p_ = PHASE_OF(c);                                                               \
+    const int K_ = STREAM_FIELD(p_, K);                                                       \
+    const int n0_ = STREAM_FIELD(p_, n0);                                                     \
+    const int row0_ = (STREAM_FIELD(p_, u) + (i) * STREAM_FIELD(p_, stride)) * 16;            \
+    const uint16_t* base_ = row0_ < n0_ ? STREAM_FIELD(p_, A0) + (int64_t)row0_ * K_          \
+                                        : STREAM_FIELD(p_, A1) + (int64_t)(row0_ - n0_) * K_; \
+    (out) = base_ + (p_ ? lane_off1 : lane_off0) +                                            \
+            (int64_t)(STREAM_FIELD(p_, kb0) + ((c) - STREAM_FIELD(p_, first_chunk)) * kC) *   \
+                k_mul;                                                                        \
+  } while (0)
 
-  const int64_t lane_off = a.tiled ? 8 * lane : (int64_t)lrow * K + 8 * kq;
-  const int k_mul = a.tiled ? 16 : 1;
-  const int step_stride = a.tiled ? 512 : kKStep;
-  auto unit_ptr = [&](int i, int c) {
-    const int row0 = (u + i * stride) * 16;
-    const uint16_t* base = row0 < a.n0 ? a.A0 + (int64_t)row0 * K
-                                       : a.A1 + (int64_t)(row0 - a.n0) * K;
-    return base + lane_off + (int64_t)(kb0 + c * kC) * k_mul;
-  };
   // Load cursor over (chunk, unit, step), in the order of the MFMAs; past
   // the wave's last step it stays on it (every ring slot refills).
-  int l_step = 0, l_i = 0, l_chunk = 0, l_left = total, l_ns = chunk_steps(0);
-  const uint16_t* l_ptr = unit_ptr(0, 0);
-  auto next_load = [&](uint4& q) {
-    q = load16_stream(l_ptr + l_step * step_stride);
-    if (l_left > 1) {
-      --l_left;
-      if (++l_step == l_ns) {
-        l_step = 0;
-        if (++l_i == my_units) {
-          l_i = 0;
-          ++l_chunk;
-          l_ns = chunk_steps(l_chunk);
-        }
-        l_ptr = unit_ptr(l_i, l_chunk);
-      }
-    }
-  };
+  int l_chunk = WORK_CHUNK(0);
+  int l_step = 0, l_i = 0, l_left = total, l_ns = CHUNK_STEPS(l_chunk), l_mu = UNITS_OF(l_chunk);
+  const uint16_t* l_ptr;
+  UNIT_PTR(l_chunk, 0, l_ptr);
+#define NEXT_LOAD(q)                          \
+  do {                                        \
+    (q) = load16_stream(l_ptr + l_step * step_stride); \
+    if (l_left > 1) {                         \
+      --l_left;                               \
+      if (++l_step == l_ns) {                 \
+        l_step = 0;                           \
+        if (++l_i == l_mu) {                  \
+          l_i = 0;                            \
+          l_chunk = WORK_CHUNK(l_chunk + 1);  \
+          l_ns = CHUNK_STEPS(l_chunk);        \
+          l_mu = UNITS_OF(l_chunk);           \
+        }                                     \
+        UNIT_PTR(l_chunk, l_i, l_ptr);        \
+      }                                       \
+    }                                         \
+  } while (0)
   uint4 ra[kPF];
 #pragma unroll
-  for (int i = 0; i < kPF; ++i) next_load(ra[i]);
+  for (int i = 0; i < kPF; ++i) NEXT_LOAD(ra[i]);
 
+  // hold slots: phase 0's units first, then phase 1's
   f32x4_t acc[NT];
   f32x4_t hold[kMaxU][NT];
 #pragma unroll
@@ -625,10 +718,13 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a, int block) {
   for (int j = 0; j < kMaxU; ++j)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) hold[j][nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  int c_chunk = WORK_CHUNK(0);
+  int c_step = 0, c_i = 0, c_ns = CHUNK_STEPS(c_chunk), c_mu = UNITS_OF(c_chunk);
+  int c_slot0 = SLOT_BASE(c_chunk);
   // operand reads: token row 16 nt + lrow, piece (4 step + kq) ^ lrow
-  int c_step = 0, c_i = 0, c_chunk = 0, c_ns = chunk_steps(0);
-  const uint16_t* xrow = xs + lrow * kC;
-  wait_filled(flags, 1);
+  const uint16_t* xrow = xs + (c_chunk % kRing) * kChunkElems + lrow * kC;
+  if (lane == 0) flag_set(flags + 1 + wave, c_chunk);
+  wait_filled(flags, c_chunk + 1);
 
   for (int q0 = 0; q0 < total; q0 += kPF) {
 #pragma unroll
@@ -643,46 +739,77 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a, int block) {
               0, 0);
         }
         if (++c_step == c_ns) {
-          // park this unit's sum, take up the next one's (register moves:
-          // the slot index is wave-uniform)
           c_step = 0;
-          const int next_i = c_i + 1 == my_units ? 0 : c_i + 1;
+          int next_i = c_i + 1;
+          int next_chunk = c_chunk;
+          if (next_i == c_mu) {
+            // this wave is done with the chunk: its buffer may be refilled
+            next_i = 0;
+            next_chunk = WORK_CHUNK(c_chunk + 1);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) flag_set(flags + 1 + wave, next_chunk);
+          }
+          // park this unit's sum, take up the next one's (register moves:
+          // the slot indices are wave-uniform)
+          const int here = c_slot0 + c_i;
+          if (next_chunk < nchunks) {
+            c_ns = CHUNK_STEPS(next_chunk);
+            c_mu = UNITS_OF(next_chunk);
+            c_slot0 = SLOT_BASE(next_chunk);
+          }
+          const int there = c_slot0 + next_i;
 #pragma unroll
           for (int j = 0; j < kMaxU; ++j)
-            if (j == c_i)
+            if (j == here)
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) hold[j][nt] = acc[nt];
 #pragma unroll
           for (int j = 0; j < kMaxU; ++j)
-            if (j == next_i)
+            if (j == there)
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) acc[nt] = hold[j][nt];
           c_i = next_i;
-          if (c_i == 0) {
-            // this wave is done with the chunk: its buffer may be refilled
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            ++c_chunk;
-            if (lane == 0) flag_set(flags + 1 + wave, c_chunk);
+          if (next_chunk != c_chunk) {
+            c_chunk = next_chunk;
             if (c_chunk < nchunks) {
-              c_ns = chunk_steps(c_chunk);
               xrow = xs + (c_chunk % kRing) * kChunkElems + lrow * kC;
               wait_filled(flags, c_chunk + 1);
             }
           }
         }
       }
-      next_load(ra[i]);
+      NEXT_LOAD(ra[i]);
     }
   }
-  const int ntiles = a.N / 16;
-#pragma unroll
-  for (int j = 0; j < kMaxU; ++j)
-    if (j < my_units)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        a.partials[(((int64_t)split * ntiles + u + j * stride) * NT + nt) * kWave + lane] =
-            hold[j][nt];
+  // Accumulator lane layout: rows 16 * tile + 4 * (lane / 16) + v, token
+  // 16 * nt + lane % 16; one 1 KB store per (tile, token block).  Hold slot
+  // k is unit k - s0 of its phase (slots visited in a static order: a
+  // run-time index into hold would put it in scratch memory).
+#define STORE_PHASE(q, s0)                                                                    \
+  do {                                                                                        \
+    const int ntiles_ = (q).N / 16;                                                           \
+    _Pragma("unroll") for (int k = 0; k < kMaxU; ++k) {                                       \
+      const int j = k - (s0);                                                                 \
+      if (j >= 0 && j < (q).units)                                                            \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                     \
+            (q).partials[(((int64_t)(q).split * ntiles_ + (q).u + j * (q).stride) * NT + nt) * \
+                             kWave + lane] = hold[k][nt];                                     \
+    }                                                                                         \
+  } while (0)
+  STORE_PHASE(ph0, 0);
+  if (kPhases > 1) STORE_PHASE(ph1, q0_units);
+#undef PHASE_OF
+#undef CHUNK_STEPS
+#undef UNITS_OF
+#undef SKIP0
+#undef WORK_CHUNK
+#undef SLOT_BASE
+#undef UNIT_PTR
+#undef NEXT_LOAD
+#undef STORE_PHASE
 }
+#undef STREAM_FIELD
+#undef STREAM_LOCALS
 
 // Blocks reach the 8 XCDs in turn (block g on XCD g % 8), and each XCD has
 // its own L2.  The position of block g among the blocks [s, s + m) sorted
@@ -738,20 +865,18 @@ __global__ void __launch_bounds__(kWave * kWaves) px_group_mp_kernel(FxArgs a0, 
     px_body_mp<NT, kWaves, kMaxU>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
 }
 
+
 template <int NT, int kW, int kPF, int kMaxU>
 __global__ void __launch_bounds__(kWave * (kW + 1)) px_stream_kernel(FxArgs a) {
-  px_body_stream<NT, kW, kPF, kMaxU>(a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
+  px_body_stream<NT, kW, kPF, kMaxU, 1>(a, a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
 }
 
-// Two independent projections in one streamed grid (the fused tail's down
-// and up projections).
+// Two projections (the fused tail's down and up) in one streamed grid:
+// block g runs split g / bps of each, one after the other.
 template <int NT, int kW, int kPF, int kMaxU>
-__global__ void __launch_bounds__(kWave * (kW + 1)) px_group_stream_kernel(FxArgs a0, FxArgs a1,
-                                                                         int blocks0) {
-  if ((int)blockIdx.x < blocks0)
-    px_body_stream<NT, kW, kPF, kMaxU>(a0, xcd_position(blockIdx.x, 0, blocks0));
-  else
-    px_body_stream<NT, kW, kPF, kMaxU>(a1, xcd_position(blockIdx.x, blocks0, fx_blocks(a1)));
+__global__ void __launch_bounds__(kWave * (kW + 1)) px_pair_stream_kernel(FxArgs a0, FxArgs a1) {
+  const int g0 = fx_blocks(a0), g1 = fx_blocks(a1);
+  px_body_stream<NT, kW, kPF, kMaxU, 2>(a0, a1, xcd_position(blockIdx.x, 0, g0 > g1 ? g0 : g1));
 }
 
 // Slice partials added in slice order, then the epilogue: one thread per
@@ -1322,27 +1447,34 @@ hipError_t group_mp_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan
 }
 
 template <int NT, int W, int PF, int U>
-hipError_t group_stream_launch(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
-                               hipStream_t s) {
+hipError_t pair_stream_launch(const FxArgs& a0, const FxArgs& a1, int blocks, hipStream_t s) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = allow_full_lds(
-      reinterpret_cast<const void*>(px_group_stream_kernel<NT, W, PF, U>), lds_set);
+      reinterpret_cast<const void*>(px_pair_stream_kernel<NT, W, PF, U>), lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((px_group_stream_kernel<NT, W, PF, U>), dim3(blocks), dim3(kWave * (W + 1)),
-                     kStreamLds, s, a0, a1, blocks0);
+  hipLaunchKernelGGL((px_pair_stream_kernel<NT, W, PF, U>), dim3(blocks), dim3(kWave * (W + 1)),
+                     kStreamLds, s, a0, a1);
   return hipGetLastError();
 }
 
-// 7 consumer waves holding up to 2 units each.
-hipError_t group_stream_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g,
-                                 int blocks0, int blocks, hipStream_t s) {
-  if (g.waves != 7 || g.hold > 2) return hipErrorInvalidValue;  // not planned
+// One unit of each projection a wave, 6 or 7 consumer waves.
+template <int W>
+hipError_t pair_stream_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks,
+                                   hipStream_t s) {
   switch (token_blocks(a0.b)) {
-    case 1: return group_stream_launch<1, 7, 16, 2>(a0, a1, blocks0, blocks, s);
-    case 2: return group_stream_launch<2, 7, 16, 2>(a0, a1, blocks0, blocks, s);
-    case 4: return group_stream_launch<4, 7, 16, 2>(a0, a1, blocks0, blocks, s);
-    default: return group_stream_launch<8, 7, 16, 2>(a0, a1, blocks0, blocks, s);
+    case 1: return pair_stream_launch<1, W, 16, 2>(a0, a1, blocks, s);
+    case 2: return pair_stream_launch<2, W, 16, 2>(a0, a1, blocks, s);
+    case 4: return pair_stream_launch<4, W, 16, 2>(a0, a1, blocks, s);
+    default: return pair_stream_launch<8, W, 16, 2>(a0, a1, blocks, s);
   }
+}
+
+hipError_t pair_stream_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g,
+                                int blocks, hipStream_t s) {
+  if (g.hold != 2) return hipErrorInvalidValue;  // not planned
+  if (g.waves == 6) return pair_stream_dispatch_nt<6>(a0, a1, blocks, s);
+  if (g.waves == 7) return pair_stream_dispatch_nt<7>(a0, a1, blocks, s);
+  return hipErrorInvalidValue;
 }
 
 template <int W, int H>
@@ -1425,17 +1557,19 @@ GroupPlan plan_group_mp(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1
   return best;
 }
 
-// Both streamed: each keeps its K ranges; blocks per split the fewest that
-// give every wave at most 2 units (7 consumer waves), both grids on the CUs.
+// Both streamed with the same consumer waves: one grid in which block g
+// runs split g / bps of each plan in turn, each wave one unit of each (the
+// plans' own blocks per split and K ranges, so the sums of the plans' own
+// launches).  The grid is the larger of the two; none when it exceeds the
+// CUs.
 GroupPlan plan_group_stream(const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
   const int cu = device_cu_count();
-  constexpr int kW = 7, kU = 2;
-  const int bps0 = (rows0 / 16 + kW * kU - 1) / (kW * kU);
-  const int bps1 = (rows1 / 16 + kW * kU - 1) / (kW * kU);
-  if (bps0 * p0.splits + bps1 * p1.splits > cu) return GroupPlan{};
-  const int pw0 = (rows0 / 16 + bps0 * kW - 1) / (bps0 * kW);
-  const int pw1 = (rows1 / 16 + bps1 * kW - 1) / (bps1 * kW);
-  return GroupPlan{bps0, bps1, kW, pw0 > pw1 ? pw0 : pw1, 0, 1};
+  if (p0.waves != p1.waves || p0.hold != 1 || p1.hold != 1) return GroupPlan{};
+  if (p0.blocks_per_slice * p0.splits > cu || p1.blocks_per_slice * p1.splits > cu)
+    return GroupPlan{};
+  (void)rows0;
+  (void)rows1;
+  return GroupPlan{p0.blocks_per_slice, p1.blocks_per_slice, p0.waves, 2, 0, 1};
 }
 
 GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, int rows1) {
@@ -1498,7 +1632,8 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   const int blocks = blocks0 + g.bps1 * up.splits;
   const size_t lds = down.lds > up.lds ? down.lds : up.lds;
   if (g.stream) {
-    e = group_stream_dispatch(dn, upa, g, blocks0, blocks, s);
+    const int g0 = g.bps0 * down.splits, g1 = g.bps1 * up.splits;
+    e = pair_stream_dispatch(dn, upa, g, g0 > g1 ? g0 : g1, s);
   } else if (!g.waves) {
     // no grid holds both (8 token blocks, one unit a wave): two launches of
     // the same plans, so the same sums

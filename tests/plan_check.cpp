@@ -91,14 +91,20 @@ void check_group(int b, int H, int I, int L, const ProjTuning& td, const ProjTun
   if (must_exist) CHECK(g.waves > 0, CTX);
   if (!g.waves) return;
   CHECK(g.bps0 >= 1 && g.bps1 >= 1, CTX);
-  CHECK(g.bps0 * dn.splits + g.bps1 * up.splits <= device_cu_count(), CTX);
   const int pw0 = ceil_div(H / 16, g.bps0 * g.waves);
   const int pw1 = ceil_div(H / 16, g.bps1 * g.waves);
   if (g.stream) {
-    // both streamed, 7 consumer waves holding up to 2 units
-    CHECK(dn.stream && up.stream && g.waves == 7, CTX);
-    CHECK(pw0 <= g.hold && pw1 <= g.hold && g.hold <= 2, CTX);
-  } else if (g.mp) {
+    // both streamed: one grid running each plan's own splits in turn, one
+    // unit of each a wave
+    CHECK(dn.stream && up.stream && g.waves == dn.waves && g.waves == up.waves, CTX);
+    CHECK(g.bps0 == dn.blocks_per_slice && g.bps1 == up.blocks_per_slice && g.hold == 2, CTX);
+    CHECK(pw0 <= 1 && pw1 <= 1, CTX);
+    CHECK(g.bps0 * dn.splits <= device_cu_count() && g.bps1 * up.splits <= device_cu_count(),
+          CTX);
+    return;
+  }
+  CHECK(g.bps0 * dn.splits + g.bps1 * up.splits <= device_cu_count(), CTX);
+  if (g.mp) {
     CHECK(dn.passes > 1 || up.passes > 1, CTX);
     CHECK(g.waves == 8 || g.waves == 12, CTX);
     CHECK(pw0 <= g.hold && pw1 <= g.hold && g.hold <= 4, CTX);

@@ -1101,7 +1101,7 @@ ProjPlan make_mp_plan(int b, int rows, int K, const ProjTuning& t) {
 struct StreamShape {
   int waves, pf, units;
 };
-constexpr StreamShape kStreamShapes[] = {{6, 16, 1}, {7, 16, 1}};
+constexpr StreamShape kStreamShapes[] = {{6, 8, 1}, {7, 8, 1}};
 
 // The streamed plan: `splits` K ranges (multiples of the k step; the last
 // may be shorter), the CUs shared evenly between them, every wave of a
@@ -1363,9 +1363,9 @@ hipError_t stream_dispatch_nt(const FxArgs& a, const ProjPlan& p, hipStream_t s)
 }
 
 hipError_t stream_dispatch(const FxArgs& a, const ProjPlan& p, hipStream_t s) {
-  if (!a.partials || p.hold != 1 || p.pf != 16) return hipErrorInvalidValue;  // not planned
-  if (p.waves == 6) return stream_dispatch_nt<6, 16, 1>(a, p, s);
-  if (p.waves == 7) return stream_dispatch_nt<7, 16, 1>(a, p, s);
+  if (!a.partials || p.hold != 1 || p.pf != 8) return hipErrorInvalidValue;  // not planned
+  if (p.waves == 6) return stream_dispatch_nt<6, 8, 1>(a, p, s);
+  if (p.waves == 7) return stream_dispatch_nt<7, 8, 1>(a, p, s);
   return hipErrorInvalidValue;
 }
 
@@ -1462,10 +1462,10 @@ template <int W>
 hipError_t pair_stream_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks,
                                    hipStream_t s) {
   switch (token_blocks(a0.b)) {
-    case 1: return pair_stream_launch<1, W, 16, 2>(a0, a1, blocks, s);
-    case 2: return pair_stream_launch<2, W, 16, 2>(a0, a1, blocks, s);
-    case 4: return pair_stream_launch<4, W, 16, 2>(a0, a1, blocks, s);
-    default: return pair_stream_launch<8, W, 16, 2>(a0, a1, blocks, s);
+    case 1: return pair_stream_launch<1, W, 8, 2>(a0, a1, blocks, s);
+    case 2: return pair_stream_launch<2, W, 8, 2>(a0, a1, blocks, s);
+    case 4: return pair_stream_launch<4, W, 8, 2>(a0, a1, blocks, s);
+    default: return pair_stream_launch<8, W, 8, 2>(a0, a1, blocks, s);
   }
 }
 

@@ -44,12 +44,12 @@ ProjPlan check_plan(int b, int rows, int K, bool always, const ProjTuning& t, co
   CHECK(p.k_per_split > 0 && p.k_per_split % 32 == 0, CTX);
   if (p.stream) {
     // the streamed kernel: activations through the LDS chunk ring (fixed
-    // LDS), K ranges that cover K, 6 or 7 consumer waves with a 16-deep
+    // LDS), K ranges that cover K, 6 or 7 consumer waves with an 8-deep
     // ring, one unit a wave
     CHECK(p.lds == 4 * 32 * 1024 + 256, CTX);
     CHECK((p.splits - 1) * p.k_per_split < K && K <= p.splits * p.k_per_split, CTX);
     CHECK(p.blocks_per_slice >= 1 && p.splits * p.blocks_per_slice <= target, CTX);
-    CHECK((p.waves == 6 || p.waves == 7) && p.pf == 16 && p.mr == 1 && p.hold == 1, CTX);
+    CHECK((p.waves == 6 || p.waves == 7) && p.pf == 8 && p.mr == 1 && p.hold == 1, CTX);
     CHECK(ceil_div(rows / 16, p.blocks_per_slice * p.waves) <= 1, CTX);
     CHECK(rows % 16 == 0 && K % 8 == 0, CTX);
     return p;

@@ -980,6 +980,28 @@ def test_decode_tail_ragged(b, K, tp, L, H, I, layout):
         assert np.array_equal(fused[key], calls[key]), key
 
 
+@pytest.mark.parametrize("mode", [mt.NORM_GAIN_AFTER, mt.NORM_GAIN_FIRST, mt.NO_NORM])
+@pytest.mark.parametrize("wkey", ["w32", "w16"])
+def test_decode_tail_finalize_waves_every_mode(mode, wkey):
+    """The decode tail at the tail's real sizes (b=16): the rank partials are
+    the oracle's bit for bit in every norm mode and route-weight type, and
+    every output equals the two separate calls."""
+    ep = workloads.ep_finalize(40 + mode, b=16)
+    up = workloads.upproj(41, b=16)
+    sh = workloads.shared(42, b=16)
+    fused, calls = run_decode_tail(ep, up, sh, mode, wkey)
+    if mode == mt.NO_NORM:
+        want, _ = oracle.finalize_plain(ep["rows"], ep["idx"], ep[wkey], combine=False,
+                                        nthreads=NT)
+    else:
+        want, _ = oracle.finalize(ep["rows"], ep["idx"], ep[wkey], ep["gamma"], ep["gain_center"],
+                                  ep["eps"], mode == mt.NORM_GAIN_FIRST, combine=False,
+                                  nthreads=NT)
+    assert np.array_equal(fused["lat"], want)
+    for key in ("lat", "out", "rs", "normed", "h"):
+        assert np.array_equal(fused[key], calls[key]), key
+
+
 def test_decode_tail_bench_config_against_oracle():
     """The benchmark's launch configuration -- moetail_decode_tail at b=64 on
     tiled weights, c2 rows into c4/c5's tail -- against the oracle: the rank

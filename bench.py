@@ -52,14 +52,15 @@ def graph_steps(steps: int) -> int:
     return max(g for g in range(1, min(steps, MAX_GRAPH_STEPS) + 1) if steps % g == 0)
 
 
-# HBM bytes of one moetail_tail call at b=64 (its four kernels), from two
-# rocprofv3 --pmc passes over `bench.py --counters` (FETCH_SIZE, then
-# WRITE_SIZE, per dispatch, the two decode steps' tail kernels averaged),
-# scaled by what each reads for the calibration kernel (256 MiB in, 256 MiB
-# out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  They hold for the kernel sources
-# with this digest only.
-TRAFFIC = dict(source_digest="85f1dc3e03bb2535", fetch_bytes=176206 * 2 * 1024,
-               write_bytes=33223 * 1024)
+# HBM bytes of one launch of the dominant kernel -- the gate/up projection's
+# split-K stage at b=64 -- from two rocprofv3 --pmc passes over
+# `bench.py --counters` (FETCH_SIZE, then WRITE_SIZE, per dispatch, that
+# kernel's dispatches averaged), scaled by what each reads for the
+# calibration kernel (256 MiB in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE
+# x 1.0).  They hold for the kernel sources with this digest only (None:
+# not taken for these sources).
+TRAFFIC = dict(source_digest="eb3293bfc1493399", fetch_bytes=88372 * 2 * 1024,
+               write_bytes=6144 * 1024)
 
 
 def kernel_source_digest():
@@ -83,8 +84,11 @@ def algorithmic_bytes():
     fin = TP * (B * K // TP) * P * 2 + TP * B * K * 4 + B * K * 4 + P * 2 + TP * B * P * 2
     shared = 3 * H * I * 2 + B * H * 2 + B * H * 2
     upproj = TP * B * P * 2 + P * 2 + H * P * 2 + B * H * 2 + B * H * 2
+    # the gate/up projection's split-K stage: its two weight matrices and x
+    # (its FP32 partials are an artifact of the split, not counted)
+    gate_up = 2 * I * H * 2 + B * H * 2
     return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj,
-                tail=shared + upproj - B * H * 2 * 2)
+                tail=shared + upproj - B * H * 2 * 2, gate_up_stage=gate_up)
 
 
 def main():
@@ -247,25 +251,36 @@ def main():
     def time_calls(fn, reps=20):
         return graph_time(lambda i: fn(sets[i % nsets]), reps)
 
+    # The dominant kernel alone: the gate/up projection's split-K stage (one
+    # launch of the streamed projection kernel), through its own entry point.
+    gu_part = torch.empty(mt.workspace_bytes(mt.OP_PROJECTION, B, 2 * I, H, mt.PROJ_GATEUP) // 4,
+                          dtype=torch.float32, device="cuda")
+
+    def gate_up_stage(d):
+        mt.moetail_projection_partials(mt.PROJ_GATEUP, d["wg"], d["wu"], d["x"], gu_part,
+                                       w_layout=lay)
+
     per_call = {n: time_calls(f) for n, f in
                 (("finalize", finalize), ("shared_expert", shared),
-                 ("combine_norm_upproj", upproj), ("tail", tail))}
+                 ("combine_norm_upproj", upproj), ("tail", tail),
+                 ("gate_up_stage", gate_up_stage))}
     algo = algorithmic_bytes()
     entry = {n: dict(us=round(per_call[n], 2), bytes=algo[n],
                      GBps=round(algo[n] / per_call[n] / 1e3, 1),
                      frac=round(algo[n] / per_call[n] / 1e3 / HBM_PEAK_GBPS, 4))
              for n in per_call}
-    dom = "tail"
+    dom = "gate_up_stage"
     traffic = traffic_bytes = None
-    if kernel_source_digest() == TRAFFIC["source_digest"]:
+    if TRAFFIC["source_digest"] and kernel_source_digest() == TRAFFIC["source_digest"]:
         traffic_bytes = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
         traffic = round(traffic_bytes / per_call[dom] / 1e3, 1)
     roofline = dict(bound="hbm",
-                    kernel="moetail_tail at b=64 (one call, four kernels: gate/up; h and y; "
-                           "down and up projections as one grid; rs and out)",
+                    kernel="px_stream_kernel<4, 6, 8, 1>: the gate/up projection's split-K stage "
+                           "at b=64 (2 x 6144 x 7168 BF16 weights and x in, FP32 partials out), "
+                           "one launch (moetail_projection_partials)",
                     achieved=entry[dom]["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=entry[dom]["frac"], traffic=traffic, traffic_bytes=traffic_bytes,
-                    algorithmic_bytes=algo[dom])
+                    algorithmic_bytes=algo[dom], us_per_launch=entry[dom]["us"])
 
     kernels = None
     if not args.no_kernels:
@@ -463,6 +478,11 @@ def counter_workloads(sets, step, log, lay, reps=2):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
     log(f"counters: {reps} decode steps")
+    gu_part = torch.empty(mt.workspace_bytes(mt.OP_PROJECTION, B, 2 * I, H, mt.PROJ_GATEUP) // 4,
+                          dtype=torch.float32, device="cuda")
+    for _ in range(reps):
+        mt.moetail_projection_partials(mt.PROJ_GATEUP, base["wg"], base["wu"], base["x"], gu_part,
+                                       w_layout=lay)
     part = torch.empty((TP, B, P), dtype=torch.int16, device="cuda")
     out = torch.empty((B, P), dtype=torch.int16, device="cuda")
     for _ in range(reps):
@@ -502,8 +522,9 @@ def counter_workloads(sets, step, log, lay, reps=2):
     for _ in range(2):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log("counters: finalize+combine b=64, expert TP b=128, combine+norm+upproj b=32, shared "
-        "expert b=32 and b=128, calibration 2 x neg over 256 MiB in, 256 MiB out")
+    log("counters: gate/up stage b=64, finalize+combine b=64, expert TP b=128, "
+        "combine+norm+upproj b=32, shared expert b=32 and b=128, calibration 2 x neg over "
+        "256 MiB in, 256 MiB out")
 
 
 def cpu_model():

@@ -24,13 +24,15 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 NORM_GAIN_AFTER, NORM_GAIN_FIRST, NO_NORM = 0, 1, 2  # moetail_finalize norm modes
 OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL = 0, 1, 2, 3, 4
+OP_PROJECTION = 5
 W_ROWS, W_TILED = 0, 1  # weight layouts of the projections
 
 PROJ_UPPROJ, PROJ_GATEUP, PROJ_DOWN = 0, 1, 2  # projection kinds for set_projection_tuning
 
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
           "moetail_shared_expert", "moetail_tail", "moetail_decode_tail", "moetail_pack_weights",
-          "moetail_set_projection_tuning", "moetail_decode_tail_noalloc")
+          "moetail_set_projection_tuning", "moetail_decode_tail_noalloc",
+          "moetail_projection_partials")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string",
                          "moetail_plan_cache_stats", "moetail_set_tp_wait_limit")
 
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.moetail_set_tp_wait_limit.argtypes = [I64]
         L.moetail_set_tp_wait_limit.restype = None
         L.moetail_decode_tail_noalloc.argtypes = L.moetail_decode_tail.argtypes[:-3] + [P]
+        L.moetail_projection_partials.argtypes = [I32, P, P, I32, I32, P, I32, I32, P, SZ, P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
@@ -300,6 +303,33 @@ def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, s
                                      _ptr(h), _ptr(rs), int(w_layout), ws, wsb,
                                      _stream(stream, dev))
     _check(st, "moetail_shared_expert")
+
+
+def moetail_projection_partials(kind, w0, w1, x, partials, stream=None, w_layout=W_ROWS):
+    """One projection's split-K stage: kind PROJ_GATEUP with w0 = w_gate and
+    w1 = w_up [N/2, K] each (N = 2 I), or PROJ_DOWN / PROJ_UPPROJ with w0
+    [N, K] and w1 None; x [b, K].  Writes the FP32 partial sums into
+    partials (a float32 tensor of at least workspace_bytes(OP_PROJECTION, b,
+    N, K, kind) bytes) in the layout the C header gives."""
+    if x.dim() != 2 or w0.dim() != 2:
+        raise ValueError("x must be [b, K] and w0 [rows, K]")
+    b, K = x.shape
+    rows = w0.shape[0]
+    if kind == PROJ_GATEUP:
+        _expect(w1, "w1", (rows, K))
+        N = 2 * rows
+    else:
+        if w1 is not None:
+            raise ValueError("w1 is the gate/up projection's second matrix only")
+        N = rows
+    _expect(w0, "w0", (rows, K))
+    if not isinstance(partials, torch.Tensor) or partials.dtype != torch.float32:
+        raise TypeError("partials must be a float32 tensor")
+    dev = _same_device(w0, w1, x, partials)
+    st = lib().moetail_projection_partials(int(kind), _ptr(w0), _ptr(w1), N, K, _ptr(x), b,
+                                           int(w_layout), _ptr(partials),
+                                           partials.numel() * 4, _stream(stream, dev))
+    _check(st, "moetail_projection_partials")
 
 
 def _tail_shapes(latent_partials, gamma, w_up, x, w_gate, w_up_shared, w_down, out, rs, normed,

@@ -174,6 +174,7 @@ struct PlanSlot {
   UpprojLayout up;
   SharedLayout sh;
   TailLayout tail;
+  ProjPlan proj;
 };
 PlanSlot plan_slots[kPlanSlots];
 int plan_next = 0;
@@ -195,6 +196,9 @@ PlanSlot plans_for(int op, int b, int d0, int d1, int d2) {
   if (op == MOETAIL_OP_COMBINE_NORM_UPPROJ) e.up = upproj_layout(b, d0, d1);
   if (op == MOETAIL_OP_SHARED_EXPERT) e.sh = shared_layout(b, d0, d1);
   if (op == MOETAIL_OP_TAIL) e.tail = tail_layout(b, d0, d1, d2);
+  // (the stage's plan in the composite calls: partials always for gate/up)
+  if (op == MOETAIL_OP_PROJECTION)
+    e.proj = plan_projection(b, d0, d1, d2 == MOETAIL_PROJ_GATEUP, tunings[d2]);
   plan_slots[plan_next] = e;
   plan_next = (plan_next + 1) % kPlanSlots;
   return e;
@@ -207,6 +211,18 @@ SharedLayout shared_plan(int b, int H, int I) {
 }
 TailLayout tail_plan(int b, int L, int H, int I) {
   return plans_for(MOETAIL_OP_TAIL, b, L, H, I).tail;
+}
+// The projection's plan and its partial bytes (0: it writes none, or no
+// plan fits).
+ProjPlan projection_plan(int kind, int b, int N, int K, size_t* bytes) {
+  const ProjPlan p = plans_for(MOETAIL_OP_PROJECTION, b, N, K, kind).proj;
+  *bytes = p.splits ? round_up(proj_partial_bytes(p, b, N, kind == MOETAIL_PROJ_GATEUP), 256) : 0;
+  return p;
+}
+bool projection_dims_ok(int kind, int b, int N, int K) {
+  return kind >= MOETAIL_PROJ_UPPROJ && kind <= MOETAIL_PROJ_DOWN && b > 0 &&
+         b <= MOETAIL_MAX_GEMM_TOKENS && N > 0 && N % (kind == MOETAIL_PROJ_GATEUP ? 32 : 16) == 0 &&
+         K > 0 && K % 32 == 0 && K <= MOETAIL_MAX_GEMM_K;
 }
 
 }  // namespace
@@ -281,6 +297,25 @@ int moetail_combine_norm_upproj(const uint16_t* latent_partials, int tp, const u
   hipError_t e = launch_latent_norm(latent_partials, tp, b, L, gamma, eps, y, stream);
   if (e == hipSuccess) e = launch_linear(w_up, w_layout, N, L, y, b, rs, out, lay.plan, part, stream);
   return hip_status(e);
+}
+
+int moetail_projection_partials(int kind, const uint16_t* w0, const uint16_t* w1, int N, int K,
+                                const uint16_t* x, int b, int w_layout, float* partials,
+                                size_t partial_bytes, hipStream_t stream) {
+  if (kind < MOETAIL_PROJ_UPPROJ || kind > MOETAIL_PROJ_DOWN) return MOETAIL_EINVAL;
+  if (b == 0) return MOETAIL_OK;
+  if (b < 0 || N <= 0 || K <= 0 || !layout_ok(w_layout)) return MOETAIL_EINVAL;
+  if (!a16(w0) || !a16(x) || partials == nullptr || !aligned(partials, 256)) return MOETAIL_EINVAL;
+  if (kind == MOETAIL_PROJ_GATEUP ? !a16(w1) : w1 != nullptr) return MOETAIL_EINVAL;
+  if (!projection_dims_ok(kind, b, N, K)) return MOETAIL_EUNSUPPORTED;
+  size_t need = 0;
+  const ProjPlan plan = projection_plan(kind, b, N, K, &need);
+  if (need == 0) return MOETAIL_EUNSUPPORTED;
+  if (partial_bytes < need) return MOETAIL_EWORKSPACE;
+  const int n0 = kind == MOETAIL_PROJ_GATEUP ? N / 2 : N;
+  return hip_status(launch_projection_partials(w0, w1, n0, N, K, x, b,
+                                               w_layout == MOETAIL_W_TILED, plan, partials,
+                                               stream));
 }
 
 int moetail_shared_expert(const uint16_t* x, int b, int H, const uint16_t* w_gate,
@@ -477,6 +512,12 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
         return 0;
       const TailLayout l = tail_plan(b, dim0, dim1, dim2);
       return tail_ok(l) ? l.h_bytes + l.y_bytes + l.part_bytes : 0;
+    }
+    case MOETAIL_OP_PROJECTION: {
+      if (!projection_dims_ok(dim2, b, dim0, dim1)) return 0;
+      size_t bytes = 0;
+      projection_plan(dim2, b, dim0, dim1, &bytes);
+      return bytes;
     }
     case MOETAIL_OP_SHARED_EXPERT: {
       if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64 || dim0 > MOETAIL_MAX_GEMM_K ||

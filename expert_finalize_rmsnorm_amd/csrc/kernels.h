@@ -124,6 +124,12 @@ struct TailArgs {
 hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
                        const ProjPlan& up, const GroupPlan& g, hipStream_t stream);
 
+// One projection's split-K stage alone: rows [0, n0) from W0, [n0, N) from
+// W1; FP32 partials in the plan's layout.
+hipError_t launch_projection_partials(const uint16_t* W0, const uint16_t* W1, int n0, int N, int K,
+                                      const uint16_t* X, int b, int tiled, const ProjPlan& plan,
+                                      float* partials, hipStream_t stream);
+
 // The tiled copy of a [n][k] weight matrix (n % 16 == 0, k % 32 == 0).
 hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
                                hipStream_t stream);

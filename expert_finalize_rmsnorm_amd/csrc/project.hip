@@ -1685,6 +1685,14 @@ hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint1
   return hipGetLastError();
 }
 
+hipError_t launch_projection_partials(const uint16_t* W0, const uint16_t* W1, int n0, int N, int K,
+                                      const uint16_t* X, int b, int tiled, const ProjPlan& plan,
+                                      float* partials, hipStream_t s) {
+  FxArgs a{W0, W1, n0, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,
+           reinterpret_cast<f32x4_t*>(partials), nullptr, nullptr, tiled};
+  return fx_dispatch(a, plan, s);
+}
+
 hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
                           const uint16_t* X, int b, uint16_t* h, const ProjPlan& plan,
                           float* partials, hipStream_t s) {

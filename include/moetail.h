@@ -67,6 +67,7 @@ extern "C" {
 #define MOETAIL_OP_COMBINE_NORM_UPPROJ 2
 #define MOETAIL_OP_SHARED_EXPERT 3
 #define MOETAIL_OP_TAIL 4
+#define MOETAIL_OP_PROJECTION 5
 
 /* Projection kinds of moetail_set_projection_tuning. */
 #define MOETAIL_PROJ_UPPROJ 0 /* the up projection (moetail_combine_norm_upproj, the tail's) */
@@ -210,6 +211,37 @@ int moetail_shared_expert(const uint16_t* x, int b, int H,
                           hipStream_t stream);
 
 /*
+ * One skinny projection's split-K stage alone ([tail_runtime] module
+ * docstring: "the K-split up projection"; [shared] SharedUmma: the gate/up
+ * and down products), the stage that dominates moetail_shared_expert and
+ * moetail_tail, for a caller that forms its own epilogue from the FP32
+ * partial sums (an expert GEMM epilogue, say) and for timing the stage:
+ *     partial[s][t][r] = sum over k in K range s, in k order, of
+ *                        fp32 W[r][k] * fp32 x[t][k]        (FP32 accumulation)
+ * with the plan of that stage in those calls (the same K ranges), so the
+ * same partial sums.  Adding them in split order from +0 gives the sums
+ * those calls round.
+ *
+ *   kind     MOETAIL_PROJ_GATEUP: w0 = w_gate, w1 = w_upw, each [N/2][K] BF16
+ *            (rows [0, N/2) of the output are gate rows, [N/2, N) up rows);
+ *            MOETAIL_PROJ_DOWN or MOETAIL_PROJ_UPPROJ: w0 [N][K], w1 NULL.
+ *   x        [b][K] BF16.   w_layout MOETAIL_W_ROWS or MOETAIL_W_TILED.
+ *   partials FP32, at least moetail_workspace_bytes(MOETAIL_OP_PROJECTION, b,
+ *            N, K, kind) bytes, 256-byte aligned; the splits S are that size
+ *            over N * T * 4, T = b rounded up to 16, 32, 64 or 128 tokens.
+ *            Split s, row r, token t sits at float index
+ *              4 * (((s * (N / 16) + r / 16) * (T / 16) + t / 16) * 64
+ *                   + 16 * ((r % 16) / 4) + t % 16) + r % 4
+ *            (the matrix cores' accumulator order); tokens t >= b hold token
+ *            b - 1's sums.
+ *   Limits: b <= 128, N % 16 == 0 (N % 32 with MOETAIL_PROJ_GATEUP),
+ *           K % 32 == 0, K <= MOETAIL_MAX_GEMM_K.
+ */
+int moetail_projection_partials(int kind, const uint16_t* w0, const uint16_t* w1, int N,
+                                int K, const uint16_t* x, int b, int w_layout, float* partials,
+                                size_t partial_bytes, hipStream_t stream);
+
+/*
  * The decode tail after the finalize in one call ([tail_runtime] module
  * docstring: the latent combine, RMSNorm and K-split up projection with the
  * shared expert's reduce-scatter partial added; [shared] for that partial):
@@ -331,6 +363,7 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
  *   MOETAIL_OP_COMBINE_NORM_UPPROJ: dim0 = L, dim1 = N, dim2 = tp
  *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
  *   MOETAIL_OP_TAIL:                dim0 = L, dim1 = H, dim2 = I
+ *   MOETAIL_OP_PROJECTION:          dim0 = N, dim1 = K, dim2 = kind
  * Returns 0 for an unknown op or out-of-range sizes.
  */
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);

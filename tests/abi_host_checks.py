@@ -170,6 +170,45 @@ def test_shared_validation():
     assert _sh(lay=5) == mt.EINVAL
 
 
+def _proj(**kw):
+    a = dict(kind=mt.PROJ_GATEUP, w0=A, w1=A, N=12288, K=7168, x=A, b=64, lay=mt.W_TILED,
+             part=A, pb=1 << 31)
+    a.update(kw)
+    return mt.lib().moetail_projection_partials(a["kind"], a["w0"], a["w1"], a["N"], a["K"],
+                                                a["x"], a["b"], a["lay"], a["part"], a["pb"],
+                                                None)
+
+
+def test_projection_partials_validation():
+    assert _proj(b=0) == mt.OK
+    assert _proj(kind=3) == mt.EINVAL
+    assert _proj(kind=-1, b=0) == mt.EINVAL  # the kind first
+    assert _proj(w1=None) == mt.EINVAL       # gate/up takes both matrices
+    assert _proj(kind=mt.PROJ_DOWN, N=7168, K=6144) == mt.EINVAL  # ... the others one
+    assert _proj(x=A + 2) == mt.EINVAL
+    assert _proj(part=A + 16) == mt.EINVAL   # 256-byte aligned partials
+    assert _proj(lay=7) == mt.EINVAL
+    assert _proj(N=12304) == mt.EUNSUPPORTED  # gate/up rows: two halves of whole tiles
+    assert _proj(K=7176) == mt.EUNSUPPORTED
+    assert _proj(b=129) == mt.EUNSUPPORTED
+    need = mt.workspace_bytes(mt.OP_PROJECTION, 64, 12288, 7168, mt.PROJ_GATEUP)
+    assert _proj(pb=need - 1) == mt.EWORKSPACE
+
+
+@pytest.mark.parametrize("b", [1, 16, 64, 128])
+def test_projection_partial_bytes(b):
+    """The partials are splits x N rows x the padded tokens in FP32, with the
+    splits of the composite calls' plans."""
+    T = 16 * next(n for n in (1, 2, 4, 8) if b <= 16 * n)
+    for kind, N, K in ((mt.PROJ_GATEUP, 12288, 7168), (mt.PROJ_DOWN, 7168, 6144),
+                       (mt.PROJ_UPPROJ, 7168, 3584)):
+        n = mt.workspace_bytes(mt.OP_PROJECTION, b, N, K, kind)
+        assert n > 0 and n % (N * T * 4) == 0, (kind, n)
+        assert 1 <= n // (N * T * 4) <= 64
+    assert mt.workspace_bytes(mt.OP_PROJECTION, b, 12288, 7168, 7) == 0
+    assert mt.workspace_bytes(mt.OP_PROJECTION, b, 12304, 7168, mt.PROJ_GATEUP) == 0
+
+
 def _tail(ws=A, wsb=1 << 31, **kw):
     a = dict(lat=A, tp=8, gamma=A, eps=1e-6, wup=A, L=3584, x=A, wg=A, wu=A, wd=A, H=7168,
              I=6144, b=64, out=A, rs=None, normed=None, h=None, lay=mt.W_TILED)

@@ -73,6 +73,19 @@ def test_shared_shapes():
         expect_shape_error(mt.moetail_shared_expert, name, **dict(good, **{name: bad}))
 
 
+def test_projection_partials_shapes():
+    good = dict(kind=mt.PROJ_GATEUP, w0=z(64, 128), w1=z(64, 128), x=z(4, 128),
+                partials=z(1024, dtype=torch.float32))
+    with pytest.raises(ValueError, match="device tensors"):
+        mt.moetail_projection_partials(**good)
+    expect_shape_error(mt.moetail_projection_partials, "w1", **dict(good, w1=z(64, 64)))
+    expect_shape_error(mt.moetail_projection_partials, "w1", **dict(good, w1=None))
+    with pytest.raises(ValueError, match="second matrix"):
+        mt.moetail_projection_partials(**dict(good, kind=mt.PROJ_DOWN))
+    with pytest.raises(TypeError, match="float32"):
+        mt.moetail_projection_partials(**dict(good, partials=z(1024)))
+
+
 def tail_args():
     return dict(latent_partials=z(2, 4, 64), gamma=z(64), eps=1e-6, w_up=z(128, 64),
                 x=z(4, 128), w_gate=z(64, 128), w_up_shared=z(64, 128), w_down=z(128, 64),

@@ -914,6 +914,69 @@ def test_tiled_weights_same_bits_tail(b, tp, L, H, I):
         assert np.array_equal(fused[key], calls[key]), key
 
 
+# ------------------------------------------------ projection partials --
+
+def partial_sums(part, kind_rows, b):
+    """The FP32 partials of moetail_projection_partials as [splits][b][N]
+    (the accumulator layout the header gives), padded tokens dropped."""
+    N = kind_rows
+    T = 16 * next(n for n in (1, 2, 4, 8) if b <= 16 * n)
+    a = part.reshape(-1, N // 16, T // 16, 4, 16, 4)  # s, tile, tok block, row quad, tok, row
+    a = a.transpose(0, 2, 4, 1, 3, 5).reshape(-1, T, N)
+    return a[:, :b, :]
+
+
+@pytest.mark.parametrize("b", [1, 32, 64])
+def test_projection_partials_up_against_oracle(b):
+    """The up projection's split-K stage alone: the partials added in split
+    order, rounded to BF16, are the oracle's out (y = the oracle's normed
+    input, no rs) within the GEMM bar."""
+    up = workloads.upproj(80 + b, b=b)
+    want_n, want_o = oracle.combine_norm_upproj(up["lat"], up["gamma"], up["eps"], up["w_up"],
+                                                None, nthreads=NT)
+    w = mt.pack_weights(dev(up["w_up"]))
+    x = dev(want_n)
+    N, K = up["w_up"].shape
+    n = mt.workspace_bytes(mt.OP_PROJECTION, b, N, K, mt.PROJ_UPPROJ)
+    part = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    mt.moetail_projection_partials(mt.PROJ_UPPROJ, w, None, x, part, w_layout=mt.W_TILED)
+    sums = partial_sums(part.cpu().numpy(), N, b)
+    acc = np.zeros((b, N), np.float32)
+    for s_ in sums:
+        acc = acc + s_
+    acc[acc == 0] = 0.0  # -0 as +0, as the calls write
+    gemm_bar(oracle.bf16_round(acc), want_o, "partials out")
+
+
+def test_projection_partials_are_the_shared_experts():
+    """The down projection's partials of moetail_projection_partials, added
+    in split order from +0 and rounded to BF16 (-0 as +0), are the rs that
+    moetail_shared_expert returns for the same h: the same stage, the same
+    sums, bit for bit."""
+    b = 64
+    sh = workloads.shared(85, b=b)
+    wg, wu, wd = (mt.pack_weights(dev(a)) for a in (sh["w_gate"], sh["w_up"], sh["w_down"]))
+    x = dev(sh["x"])
+    H, I = sh["H"], sh["I"]
+    h, rs = empty_bf16(b, I), empty_bf16(b, H)
+    ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
+    mt.moetail_shared_expert(x, wg, wu, wd, rs, h=h, workspace=ws, w_layout=mt.W_TILED)
+    n = mt.workspace_bytes(mt.OP_PROJECTION, b, H, I, mt.PROJ_DOWN)
+    part = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    mt.moetail_projection_partials(mt.PROJ_DOWN, wd, None, h, part, w_layout=mt.W_TILED)
+    sums = partial_sums(part.cpu().numpy(), H, b)
+    acc = np.zeros((b, H), np.float32)
+    for s_ in sums:
+        acc = acc + s_
+    acc[acc == 0] = 0.0  # -0 as +0
+    assert np.array_equal(oracle.bf16_round(acc), host(rs))
+    # gate/up: both matrices, the same call shape
+    n = mt.workspace_bytes(mt.OP_PROJECTION, b, 2 * I, H, mt.PROJ_GATEUP)
+    part = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    mt.moetail_projection_partials(mt.PROJ_GATEUP, wg, wu, x, part, w_layout=mt.W_TILED)
+    assert np.isfinite(part.cpu().numpy()).all()
+
+
 # ------------------------------------------------- the fused decode tail --
 
 def run_decode_tail(ep, up, sh, mode, wkey="w32", layout=mt.W_TILED):

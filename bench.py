@@ -17,14 +17,21 @@ it as moetail_finalize then moetail_tail (the same five launches), --tail
 calls as moetail_finalize and the tail's two entry points (eight launches):
 the same bits every way.
 
-Steps replay HIP graphs of the calls in order on one stream, eight steps
-(the two input sets alternating) per graph
-(--tail calls --streams 2 puts the finalize on a side stream beside the
-shared expert: measured slower, the cross-stream fork and join inside the
-graph cost more than the overlap gains); two input sets (weights and rows)
-alternate so that the 315 MB of weights per step stream from HBM, not from
-the 256 MB Infinity Cache.  Inputs are resident in HBM before the
-timed region starts.  Rank 0 prints one JSON line (progress goes to stderr).
+The timed steps replay one HIP graph of G steps on one stream, G the
+largest divisor of the step count up to 40 (a replay boundary costs about
+8 us of launch, paid once per graph), the two input sets (weights and rows)
+alternating so that the 315 MB of weights per step stream from HBM, not
+from the 256 MB Infinity Cache.  (--tail calls --streams 2 puts the finalize
+on a side stream beside the shared expert: measured slower, the cross-stream
+fork and join inside the graph cost more than the overlap gains.)  Inputs
+are resident in HBM before the timed region starts.
+
+The line's roofline object is the step's dominant kernel, the gate/up
+projection's split-K stage, timed alone with HIP events through
+moetail_projection_partials; every entry point's time and fraction, the
+per-config kernels, the targets, a same-size device copy and the CPU
+oracle's rate (on all of this process's host threads and on one) ride along.
+Rank 0 prints one JSON line (progress goes to stderr).
 """
 from __future__ import annotations
 

@@ -38,6 +38,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -124,11 +125,23 @@ def main():
                          "decode step at b=64; finalize+combine b=64; expert TP b=128; combine+"
                          "norm+up projection b=32; shared expert b=32 and 128), then two "
                          "launches of the 256 MiB calibration kernel; no timing, no JSON line")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        cpu_baseline_child()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the tp rank partials are a resident buffer on one device).", file=sys.stderr)
         sys.exit(2)
+    # The CPU baseline runs in a child process, started before the GPU is
+    # touched and idle until the GPU timing is done: its OpenMP threads end
+    # with it, and nothing of it outlives this process.
+    child = None
+    if not args.no_cpu_baseline and not args.counters:
+        child = subprocess.Popen([sys.executable, os.path.abspath(__file__),
+                                  "--cpu-baseline-child"], stdin=subprocess.PIPE,
+                                 stdout=subprocess.PIPE, text=True)
 
     import torch
 
@@ -157,8 +170,7 @@ def main():
                  out=torch.empty((B, H), dtype=torch.int16, device="cuda"),
                  ws_sh=mt.new_workspace(mt.OP_SHARED_EXPERT, B, H, I),
                  ws_up=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, B, P, H, TP),
-                 ws_tail=mt.new_workspace(mt.OP_TAIL, B, P, H, I),
-                 host=(ep, up, sh) if s == 0 else None)
+                 ws_tail=mt.new_workspace(mt.OP_TAIL, B, P, H, I))
         sets.append(d)
     torch.cuda.synchronize()
 
@@ -308,9 +320,12 @@ def main():
     ceiling = copy_ceiling(step_bytes)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("CPU oracle baseline")
-        cpu = cpu_baseline(sets[0]["host"], log)
+    if child is not None:
+        log("CPU oracle baseline (child process)")
+        out, _ = child.communicate("go\n", timeout=900)
+        if child.returncode != 0:
+            raise RuntimeError(f"the CPU baseline process failed ({child.returncode})")
+        cpu = json.loads(out.strip().splitlines()[-1])
 
     line = {
         "metric": METRIC,
@@ -555,6 +570,19 @@ def host_threads():
     if omp.isdigit() and int(omp) > 0:
         n = min(n, int(omp))
     return n
+
+
+def cpu_baseline_child():
+    """The CPU baseline's process: waits for a line "go" on stdin (the
+    parent's GPU timing done; end of input: exit at once), draws input set 0
+    as the parent does, times the oracle and prints the result as one JSON
+    line."""
+    if sys.stdin.readline().strip() != "go":
+        return
+    import workloads
+    host = (workloads.ep_finalize(0, b=B, K=K, P=P, tp=TP),
+            workloads.upproj(0, b=B, tp=TP, L=P, N=H), workloads.shared(0, b=B, H=H, I=I))
+    print(json.dumps(cpu_baseline(host, log)), flush=True)
 
 
 def cpu_baseline(host_inputs, log, seconds=(8.0, 10.0)):

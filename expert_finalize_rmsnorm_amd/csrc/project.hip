@@ -568,9 +568,10 @@ __device__ __forceinline__ StreamPhase stream_phase(const FxArgs& a, int block, 
   const auto q0_##f = ph0.f;       \
   const auto q1_##f = ph1.f;
 
-template <int NT, int kW, int kPhases>
-__device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const StreamPhase& ph1,
-                                                uint16_t* xs, int* flags, int nchunks) {
+// The direct loads of chunk x into its ring buffer (not waited for).
+template <int NT, int kPhases>
+__device__ __forceinline__ void stream_issue(const StreamPhase& ph0, const StreamPhase& ph1,
+                                             uint16_t* xs, int x) {
   constexpr int kC = kStreamCols<NT>;
   constexpr int kChunkElems = kStreamChunkBytes / 2;
   const int lane = threadIdx.x & (kWave - 1);
@@ -579,6 +580,27 @@ __device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const St
   STREAM_LOCALS(K)
   STREAM_LOCALS(kb0)
   STREAM_LOCALS(first_chunk)
+  const int p = (kPhases > 1 && x >= q1_first_chunk) ? 1 : 0;
+  const uint16_t* X = STREAM_FIELD(p, X);
+  const int K = STREAM_FIELD(p, K);
+  const int col0 = STREAM_FIELD(p, kb0) + (x - STREAM_FIELD(p, first_chunk)) * kC;
+  uint16_t* buf = xs + (x % kRing) * kChunkElems;
+#pragma unroll
+  for (int j = 0; j < kStreamLoads; ++j) {
+    const int e = j * 512 + lane * 8;  // element of the chunk this lane fills
+    const int t = e / kC;
+    const int s = ((e - t * kC) >> 3) ^ (t & 15);
+    const int col = min(col0 + 8 * s, K - 8);  // past the range: a valid piece, never read
+    const uint16_t* g = X + (int64_t)min(t, b - 1) * K + col;
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
+  }
+}
+
+// Chunk 0 was issued before the block's first barrier.
+template <int NT, int kW, int kPhases>
+__device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const StreamPhase& ph1,
+                                                uint16_t* xs, int* flags, int nchunks) {
+  const int lane = threadIdx.x & (kWave - 1);
   for (int x = 0; x < nchunks; ++x) {
     if (x >= kRing) {
       // buffer x % kRing is free once every consumer is done with chunk x - kRing
@@ -590,20 +612,7 @@ __device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const St
       }
       asm volatile("" ::: "memory");
     }
-    const int p = (kPhases > 1 && x >= q1_first_chunk) ? 1 : 0;
-    const uint16_t* X = STREAM_FIELD(p, X);
-    const int K = STREAM_FIELD(p, K);
-    const int col0 = STREAM_FIELD(p, kb0) + (x - STREAM_FIELD(p, first_chunk)) * kC;
-    uint16_t* buf = xs + (x % kRing) * kChunkElems;
-#pragma unroll
-    for (int j = 0; j < kStreamLoads; ++j) {
-      const int e = j * 512 + lane * 8;  // element of the chunk this lane fills
-      const int t = e / kC;
-      const int s = ((e - t * kC) >> 3) ^ (t & 15);
-      const int col = min(col0 + 8 * s, K - 8);  // past the range: a valid piece, never read
-      const uint16_t* g = X + (int64_t)min(t, b - 1) * K + col;
-      __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
-    }
+    if (x > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, x);
     // the chunk has landed in LDS, then it is published (an LDS write
     // after direct loads waits for them in any case)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -628,7 +637,13 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a
   const StreamPhase ph1 = stream_phase<NT, kW>(kPhases > 1 ? a1 : a0, block, ph0.nchunks);
   const int nchunks = ph0.nchunks + (kPhases > 1 ? ph1.nchunks : 0);
   if (threadIdx.x < 1 + kW) flag_set(flags + threadIdx.x, 0);
-  __syncthreads();
+  // The first chunk's loads go out before any weight load: the consumers'
+  // first ring loads (12 MB over the grid) would otherwise fill the memory
+  // queues ahead of them, and every consumer waits for that chunk (measured:
+  // it arrived 2.6-3.5 us into the launch).  Issued, then the block meets at
+  // an LDS-only barrier (the flags set; no wait for memory).
+  if (wave == kW && nchunks > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, 0);
+  lds_barrier();
   if (wave == kW) {
     stream_producer<NT, kW, kPhases>(ph0, ph1, xs, flags, nchunks);
     return;

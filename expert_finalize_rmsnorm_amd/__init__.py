@@ -458,8 +458,9 @@ def pack_weights(w, stream=None):
 
 def new_workspace(op: int, b: int, dim0: int, dim1: int = 0, dim2: int = 0, device="cuda"):
     """A device byte tensor sized for one call of `op` (None when none is
-    needed), zeroed (the expert-TP finalize needs its flags zero before the
-    first use; every call leaves them so)."""
+    needed), zeroed (the expert-TP finalize's flags and the tail's
+    output-tile counters must be zero before the first use; every call
+    leaves them so)."""
     n = workspace_bytes(op, b, dim0, dim1, dim2)
     if n == 0:
         return None

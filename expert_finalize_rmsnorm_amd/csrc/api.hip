@@ -140,17 +140,21 @@ SharedLayout shared_layout(int b, int H, int I) {
 struct TailLayout {
   ProjPlan gate_up, down, up;
   GroupPlan group;
-  size_t h_bytes, y_bytes, down_part_bytes, part_bytes;
+  size_t counter_bytes, h_bytes, y_bytes, down_part_bytes, part_bytes;
 };
 // The gate/up, down and up projections keep the plans of their own entry
 // points (so the sums are the same bits); down and up always go through
-// partials, since the last launch forms rs and then out.
+// partials, since rs is formed before out.  The workspace starts with the
+// output-tile counters of the launches that form their own sums (one per
+// tile of h, then of out), always at offset 0 whatever else the caller
+// passes: they are zero between calls.
 TailLayout tail_layout(int b, int L, int H, int I) {
   TailLayout l;
   l.gate_up = plan_projection(b, 2 * I, H, true, tunings[MOETAIL_PROJ_GATEUP]);
   l.down = plan_projection(b, H, I, false, tunings[MOETAIL_PROJ_DOWN]);
   l.up = plan_projection(b, H, L, false, tunings[MOETAIL_PROJ_UPPROJ]);
   l.group = (l.down.splits && l.up.splits) ? plan_group(b, l.down, H, l.up, H) : GroupPlan{};
+  l.counter_bytes = round_up(sizeof(unsigned) * (size_t)(I / 16 + H / 16), 256);
   l.h_bytes = round_up(sizeof(uint16_t) * (size_t)b * I, 256);
   l.y_bytes = round_up(sizeof(uint16_t) * (size_t)b * L, 256);
   const size_t g = proj_partial_bytes(l.gate_up, b, 2 * I, true);
@@ -362,10 +366,13 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
     return MOETAIL_EUNSUPPORTED;
   const TailLayout lay = tail_plan(b, L, H, I);
   if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
-  const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
+  const size_t need =
+      lay.counter_bytes + (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
   if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
     return MOETAIL_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  ws += lay.counter_bytes;
   uint16_t* hb = h;
   if (!hb) {
     hb = reinterpret_cast<uint16_t*>(ws);
@@ -377,7 +384,7 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
     ws += lay.y_bytes;
   }
   TailArgs a{x, w_gate, w_upw, w_down, H, I, latent_partials, tp, gamma, eps, w_up, L, b, hb, yb,
-             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout};
+             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout, counters};
   return hip_status(launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream));
 }
 
@@ -427,10 +434,13 @@ int decode_tail_impl(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
     return MOETAIL_EUNSUPPORTED;
   const TailLayout lay = tail_plan(b, L, H, I);
   if (!tail_ok(lay)) return MOETAIL_EUNSUPPORTED;
-  const size_t need = (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
-  if (need && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+  const size_t need =
+      lay.counter_bytes + (h ? 0 : lay.h_bytes) + (normed ? 0 : lay.y_bytes) + lay.part_bytes;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
     return MOETAIL_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
+  unsigned* counters = reinterpret_cast<unsigned*>(ws);
+  ws += lay.counter_bytes;
   uint16_t* hb = h;
   if (!hb) {
     hb = reinterpret_cast<uint16_t*>(ws);
@@ -442,7 +452,7 @@ int decode_tail_impl(const uint16_t* rows, int64_t rows_per_rank, const int32_t*
     ws += lay.y_bytes;
   }
   TailArgs a{x, w_gate, w_upw, w_down, H, I, latent_partials, tp, gamma, eps, w_up, L, b, hb, yb,
-             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout};
+             rs, out, reinterpret_cast<float*>(ws), lay.down_part_bytes, w_layout, counters};
   EpArgs ep{rows, rows_per_rank, permuted_idx, route_w, route_w_dtype == MOETAIL_BF16, fin_gamma,
             gain_center, fin_eps, weight_before_norm, b, K, L, tp, latent_partials, nullptr};
   hipError_t e = launch_ep_finalize(ep, stream);
@@ -511,7 +521,7 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
           dim1 % 64 || dim2 % 64 || dim1 > MOETAIL_MAX_GEMM_K || dim2 > MOETAIL_MAX_GEMM_K)
         return 0;
       const TailLayout l = tail_plan(b, dim0, dim1, dim2);
-      return tail_ok(l) ? l.h_bytes + l.y_bytes + l.part_bytes : 0;
+      return tail_ok(l) ? l.counter_bytes + l.h_bytes + l.y_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_PROJECTION: {
       if (!projection_dims_ok(dim2, b, dim0, dim1)) return 0;

@@ -120,6 +120,8 @@ struct TailArgs {
   float* partials;          // gate/up partials, then down and up partials
   size_t down_part_bytes;   // offset of the up partials
   int tiled;                // the four weights in the tiled layout
+  unsigned* counters;       // [I/16 + H/16], zero between calls (null: the
+                            // sums in launches of their own)
 };
 hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
                        const ProjPlan& up, const GroupPlan& g, hipStream_t stream);

@@ -517,6 +517,236 @@ __device__ __forceinline__ void wait_filled(int* flags, int need) {
   asm volatile("" ::: "memory");
 }
 
+// ------------------------------------------- split sums inside the launch
+//
+// A streamed launch can form its outputs itself.  Every wave writes its
+// units' FP32 partial tiles as before, then counts itself in at the output
+// tile's counter.  The wave whose arrival completes the count adds that
+// tile's partials of every split in split order from +0, with the adds and
+// the single BF16 rounding of split_reduce_kernel / tail_out_kernel, so the
+// bits are those of the separate sum launch.  It then writes the tile's BF16
+// outputs.  No wave waits for another: which wave is last is known from the
+// count alone, whatever order the waves run in.
+//
+// The splits of a tile run on different XCDs, whose L2 caches are not
+// coherent with each other.  So the partial tiles are written and read with
+// 16-byte buffer accesses carrying sc1, the cache policy this compiler gives
+// device-scope atomic loads and stores on this GPU.  All of a wave's partial
+// stores have completed (s_waitcnt vmcnt(0)) before its lane 0 adds to the
+// counter with a device-scope atomic.  The compiler's device-scope release is
+// that wait plus an L2 write-back for data written with plain stores, and
+// no such data is published here.  The last arriver sets its counter back
+// to zero, so every counter is zero between calls; the caller zeroes them
+// once, before the first call.
+enum { kFuseNone = 0, kFuseGateUp = 1, kFusePair = 2 };
+
+struct FuseArgs {
+  unsigned* counters;       // one per output tile (null: partials only)
+  uint16_t* out;            // gate/up: h [b][n0]; pair: out [b][N]
+  uint16_t* rs;             // pair: rs [b][N] (BF16 of the first sum), or null
+  int splits0, splits1;     // the two sums' splits (gate/up: the launch's, twice)
+  uint32_t bytes0, bytes1;  // the phases' partial regions (bounds of the accesses)
+  // The fused gate/up launch's last wave: the latent combine + RMSNorm of
+  // one token per block (lat null: none).
+  const uint16_t* lat;      // [tp][b][L]
+  const uint16_t* gamma;    // [L]
+  uint16_t* y;              // [b][L]
+  int tp, L;
+  float eps;
+};
+
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer builtins: sc1
+
+// A raw buffer over [base, base + bytes): accesses past the end read zero
+// and write nothing.  The last word is the 32-bit data format of a raw
+// buffer on this GPU family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t device_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4_t load_dev16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
+// Byte offset of this lane's f32x4 of partial tile `tile` of split s
+// (tile-major: [splits][tiles][NT][64]).
+template <int NT>
+__device__ __forceinline__ uint32_t partial_off(int s, int tiles, int tile, int nt, int lane) {
+  return ((((uint32_t)s * tiles + tile) * NT + nt) * kWave + lane) * 16u;
+}
+
+// Counts this wave in at counter c once its partial stores have completed;
+// true in the wave whose arrival makes `arrivals` (which sets c back to 0).
+__device__ __forceinline__ bool arrive_last(unsigned* c, int arrivals) {
+  const int lane = threadIdx.x & (kWave - 1);
+  unsigned old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readlane(old, 0);
+  const bool last = old + 1 == (unsigned)arrivals;
+  if (last && lane == 0) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Two split sums of this lane's f32x4 per token block, each in split order
+// from +0: tile ta of region ra (sa splits, tla tiles a split) and tile tb
+// of rb.  A batch's loads (both sums) all issue before its adds; indices
+// past the last split re-read it and are not added.
+template <int NT>
+__device__ __forceinline__ void two_split_sums(__amdgpu_buffer_rsrc_t ra, int sa, int tla, int ta,
+                                               __amdgpu_buffer_rsrc_t rb, int sb, int tlb, int tb,
+                                               f32x4_t (&za)[NT], f32x4_t (&zb)[NT]) {
+  constexpr int kB = NT <= 2 ? 8 : (NT == 4 ? 4 : 2);
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    za[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    zb[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int smax = sa > sb ? sa : sb;
+  for (int s0 = 0; s0 < smax; s0 += kB) {
+    f32x4_t qa[kB][NT], qb[kB][NT];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int pa = min(s0 + j, sa - 1), pb = min(s0 + j, sb - 1);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        qa[j][nt] = load_dev16(ra, partial_off<NT>(pa, tla, ta, nt, lane));
+        qb[j][nt] = load_dev16(rb, partial_off<NT>(pb, tlb, tb, nt, lane));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (s0 + j < sa) za[nt] = za[nt] + qa[j][nt];
+        if (s0 + j < sb) zb[nt] = zb[nt] + qb[j][nt];
+      }
+  }
+}
+
+// The last arriver's work for output tile t.  Gate/up: h = SiLU(gate sum) *
+// up sum (gate tiles [0, n0/16), up tiles [n0/16, N/16) of one region).
+// Pair: rs = bf16(down sum), out = bf16(up sum + rs).  -0 leaves as +0.
+// Accumulator lane layout: rows 16 t + 4 (lane / 16) + v, token
+// 16 nt + lane % 16.
+template <int NT, int kFuse>
+__device__ __forceinline__ void fuse_tile(const FxArgs& a0, const FxArgs& a1, const FuseArgs& f,
+                                          int t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  f32x4_t za[NT], zb[NT];
+  const __amdgpu_buffer_rsrc_t r0 = device_rsrc(a0.partials, f.bytes0);
+  if (kFuse == kFuseGateUp) {
+    two_split_sums<NT>(r0, f.splits0, a0.N / 16, t, r0, f.splits0, a0.N / 16, t + a0.n0 / 16, za,
+                       zb);
+  } else {
+    const __amdgpu_buffer_rsrc_t r1 = device_rsrc(a1.partials, f.bytes1);
+    two_split_sums<NT>(r0, f.splits0, a0.N / 16, t, r1, f.splits1, a1.N / 16, t, za, zb);
+  }
+  const int row = 16 * t + 4 * (lane >> 4);
+  const int nout = kFuse == kFuseGateUp ? a0.n0 : a0.N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int tok = 16 * nt + (lane & 15);
+    if (tok >= a0.b) continue;
+    const f32x4_t g = za[nt], u = zb[nt];
+    uint2* dst = reinterpret_cast<uint2*>(f.out + (int64_t)tok * nout + row);
+    if (kFuse == kFuseGateUp) {
+      *dst = pack4_pz(gated(g[0], u[0]), gated(g[1], u[1]), gated(g[2], u[2]), gated(g[3], u[3]));
+    } else {
+      const uint2 rs2 = pack4_pz(g[0], g[1], g[2], g[3]);
+      if (f.rs) *reinterpret_cast<uint2*>(f.rs + (int64_t)tok * nout + row) = rs2;
+      *dst = pack4_pz(u[0] + bf16_lo(rs2.x), u[1] + bf16_hi(rs2.x), u[2] + bf16_lo(rs2.y),
+                      u[3] + bf16_hi(rs2.y));
+    }
+  }
+}
+
+// One token's latent combine + RMSNorm by a single wave: the arithmetic of
+// latent_norm_body, whose block gives each 512-column block its own wave.
+// Here the wave takes the column blocks in turn (two blocks' loads in
+// flight), adds their butterfly totals in block order from +0 as that
+// block does, and then writes y.  L <= 8192: at most 16 column blocks, each
+// lane's rounded combine of them kept in registers.
+constexpr int kNormMaxBlocks = 16;
+__device__ __forceinline__ void latent_norm_wave(const FuseArgs& f, int b, int t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int L = f.L, tp = f.tp;
+  const int nblk = (L + kBlockCols - 1) / kBlockCols;
+  const uint16_t* src = f.lat + (int64_t)t * L;
+  const int64_t rank_stride = (int64_t)b * L;
+  uint4 lq[kNormMaxBlocks];
+  float total = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kNormMaxBlocks; j += 2) {
+    if (j >= nblk) continue;  // (not break: the loop stays fully unrolled)
+    int colc[2];
+    bool has[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = ((j + h) * kWave + lane) * kChunk;
+      has[h] = j + h < nblk && col < L;
+      colc[h] = col < L ? col : L - kChunk;
+    }
+    float sum[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[h][e] = 0.0f;
+    for (int r0 = 0; r0 < tp; r0 += 8) {
+      uint4 q[2][8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[h][u] = load16(src + min(r0 + u, tp - 1) * rank_stride + colc[h]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (r0 + u < tp) {
+            float v[8];
+            unpack8(q[h][u], v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[h][e] = sum[h][e] + v[e];
+          }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (j + h < nblk) {
+        lq[j + h] = pack8(sum[h]);
+        float lv[8];
+        unpack8(lq[j + h], lv);
+        const float s = wave_butterfly_sum(has[h] ? chunk_sum_of_squares(lv) : 0.0f);
+        total = total + s;
+      }
+    }
+  }
+  const float inv = inv_rms(total, (float)(1.0 / (double)L), f.eps);
+  uint4 gq[kNormMaxBlocks];
+#pragma unroll
+  for (int j = 0; j < kNormMaxBlocks; ++j) {
+    const int col = (j * kWave + lane) * kChunk;
+    if (j < nblk) gq[j] = load16(f.gamma + (col < L ? col : L - kChunk));
+  }
+#pragma unroll
+  for (int j = 0; j < kNormMaxBlocks; ++j) {
+    const int col = (j * kWave + lane) * kChunk;
+    if (j < nblk && col < L) {
+      float lv[8], gv[8], o[8];
+      unpack8(lq[j], lv);
+      unpack8(gq[j], gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float n = lv[e] * inv;
+        o[e] = n * gv[e];
+      }
+      store16(f.y + (int64_t)t * L + col, pack8_pz(o));
+    }
+  }
+}
+
 // One projection's share of a streamed block: its K range (split) and the
 // units of it that this wave holds.  With two phases a block runs the
 // first projection's chunks, then the second's (the fused tail's down and
@@ -622,9 +852,12 @@ __device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const St
 
 // kPhases (1 or 2) projections in one streamed block: a0's chunks, then
 // a1's (a1 unused with one phase); block: the block's position in both
-// grids.
-template <int NT, int kW, int kPF, int kMaxU, int kPhases>
-__device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a1, int block) {
+// grids.  kFuse: the split sums formed in the launch (kFuseGateUp: h, and
+// the block's wave kW + 1 forms y; kFusePair: rs and out), when f.counters
+// is set.
+template <int NT, int kW, int kPF, int kMaxU, int kPhases, int kFuse = kFuseNone>
+__device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a1, int block,
+                                               const FuseArgs& f = FuseArgs{}) {
   constexpr int kC = kStreamCols<NT>;
   constexpr int kChunkElems = kStreamChunkBytes / 2;
   extern __shared__ uint16_t xs[];
@@ -644,6 +877,11 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a
   // an LDS-only barrier (the flags set; no wait for memory).
   if (wave == kW && nchunks > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, 0);
   lds_barrier();
+  if (kFuse == kFuseGateUp && wave == kW + 1) {
+    if (f.lat)
+      for (int t = blockIdx.x; t < a0.b; t += gridDim.x) latent_norm_wave(f, a0.b, t);
+    return;
+  }
   if (wave == kW) {
     stream_producer<NT, kW, kPhases>(ph0, ph1, xs, flags, nchunks);
     return;
@@ -800,19 +1038,45 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a
   // 16 * nt + lane % 16; one 1 KB store per (tile, token block).  Hold slot
   // k is unit k - s0 of its phase (slots visited in a static order: a
   // run-time index into hold would put it in scratch memory).
-#define STORE_PHASE(q, s0)                                                                    \
+#define STORE_PHASE(q, s0, bytes)                                                             \
   do {                                                                                        \
     const int ntiles_ = (q).N / 16;                                                           \
+    const __amdgpu_buffer_rsrc_t r_ = device_rsrc((q).partials, (bytes));                     \
     _Pragma("unroll") for (int k = 0; k < kMaxU; ++k) {                                       \
       const int j = k - (s0);                                                                 \
       if (j >= 0 && j < (q).units)                                                            \
-        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                     \
-            (q).partials[(((int64_t)(q).split * ntiles_ + (q).u + j * (q).stride) * NT + nt) * \
-                             kWave + lane] = hold[k][nt];                                     \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                   \
+          const int tile_ = (q).u + j * (q).stride;                                           \
+          if (fused)                                                                          \
+            store_dev16(r_, partial_off<NT>((q).split, ntiles_, tile_, nt, lane), hold[k][nt]); \
+          else                                                                                \
+            (q).partials[(((int64_t)(q).split * ntiles_ + tile_) * NT + nt) * kWave + lane] =  \
+                hold[k][nt];                                                                  \
+        }                                                                                     \
     }                                                                                         \
   } while (0)
-  STORE_PHASE(ph0, 0);
-  if (kPhases > 1) STORE_PHASE(ph1, q0_units);
+  // (with the sums formed here, the stores are the device-coherent ones)
+  const bool fused = kFuse != kFuseNone && f.counters != nullptr;
+  STORE_PHASE(ph0, 0, f.bytes0);
+  if (kPhases > 1) STORE_PHASE(ph1, q0_units, f.bytes1);
+  if (fused) {
+    // every lane's partial stores complete, then the arrivals (one per unit
+    // held); the wave completing a tile's count forms that tile
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int arrivals = kFuse == kFuseGateUp ? 2 * f.splits0 : f.splits0 + f.splits1;
+    const int half = a0.n0 / 16;  // gate/up: up tile i + half pairs with gate tile i
+#define FUSE_PHASE(q)                                                                 \
+  _Pragma("unroll") for (int j = 0; j < kMaxU; ++j) {                                 \
+    if (j < (q).units) {                                                              \
+      int t_ = (q).u + j * (q).stride;                                                \
+      if (kFuse == kFuseGateUp && t_ >= half) t_ -= half;                             \
+      if (arrive_last(f.counters + t_, arrivals)) fuse_tile<NT, kFuse>(a0, a1, f, t_); \
+    }                                                                                 \
+  }
+    FUSE_PHASE(ph0);
+    if (kPhases > 1) FUSE_PHASE(ph1);
+#undef FUSE_PHASE
+  }
 #undef PHASE_OF
 #undef CHUNK_STEPS
 #undef UNITS_OF
@@ -886,12 +1150,29 @@ __global__ void __launch_bounds__(kWave * (kW + 1)) px_stream_kernel(FxArgs a) {
   px_body_stream<NT, kW, kPF, kMaxU, 1>(a, a, xcd_position(blockIdx.x, 0, fx_blocks(a)));
 }
 
+// The gate/up projection forming h in the launch, its blocks' last wave
+// forming y (the fused tail's first launch after the finalize).
+template <int NT, int kW, int kPF>
+__global__ void __launch_bounds__(kWave * (kW + 2)) px_gateup_fused_kernel(FxArgs a, FuseArgs f) {
+  px_body_stream<NT, kW, kPF, 1, 1, kFuseGateUp>(a, a, xcd_position(blockIdx.x, 0, fx_blocks(a)),
+                                                 f);
+}
+
 // Two projections (the fused tail's down and up) in one streamed grid:
 // block g runs split g / bps of each, one after the other.
 template <int NT, int kW, int kPF, int kMaxU>
 __global__ void __launch_bounds__(kWave * (kW + 1)) px_pair_stream_kernel(FxArgs a0, FxArgs a1) {
   const int g0 = fx_blocks(a0), g1 = fx_blocks(a1);
   px_body_stream<NT, kW, kPF, kMaxU, 2>(a0, a1, xcd_position(blockIdx.x, 0, g0 > g1 ? g0 : g1));
+}
+
+// The same grid forming rs and out in the launch (the fused tail's last).
+template <int NT, int kW, int kPF>
+__global__ void __launch_bounds__(kWave * (kW + 1)) px_pair_fused_kernel(FxArgs a0, FxArgs a1,
+                                                                        FuseArgs f) {
+  const int g0 = fx_blocks(a0), g1 = fx_blocks(a1);
+  px_body_stream<NT, kW, kPF, 2, 2, kFusePair>(a0, a1,
+                                               xcd_position(blockIdx.x, 0, g0 > g1 ? g0 : g1), f);
 }
 
 // Slice partials added in slice order, then the epilogue: one thread per
@@ -1492,6 +1773,74 @@ hipError_t pair_stream_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupP
   return hipErrorInvalidValue;
 }
 
+// The fused tail's two streamed launches (h and y; rs and out formed in the
+// launch): the plans' shapes, as pair_stream_dispatch and stream_dispatch.
+template <int NT, int W>
+hipError_t gateup_fused_launch(const FxArgs& a0, const ProjPlan& p, const FuseArgs& f,
+                               hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_gateup_fused_kernel<NT, W, 8>), lds_set);
+  if (e != hipSuccess) return e;
+  FxArgs a = a0;
+  a.passes = 1;
+  hipLaunchKernelGGL((px_gateup_fused_kernel<NT, W, 8>), dim3(p.splits * p.blocks_per_slice),
+                     dim3(kWave * (W + 2)), kStreamLds, s, a, f);
+  return hipGetLastError();
+}
+
+template <int W>
+hipError_t gateup_fused_dispatch_nt(const FxArgs& a, const ProjPlan& p, const FuseArgs& f,
+                                    hipStream_t s) {
+  switch (token_blocks(a.b)) {
+    case 1: return gateup_fused_launch<1, W>(a, p, f, s);
+    case 2: return gateup_fused_launch<2, W>(a, p, f, s);
+    case 4: return gateup_fused_launch<4, W>(a, p, f, s);
+    default: return gateup_fused_launch<8, W>(a, p, f, s);
+  }
+}
+
+// 6 consumer waves only: with 7 (9 waves a block, 168 registers a wave) the
+// y wave's registers no longer fit and spill (launch_tail takes the four
+// launches for such plans).
+hipError_t gateup_fused_dispatch(const FxArgs& a, const ProjPlan& p, const FuseArgs& f,
+                                 hipStream_t s) {
+  if (!p.stream || !a.partials || p.hold != 1 || p.pf != 8 || p.waves != 6)
+    return hipErrorInvalidValue;
+  return gateup_fused_dispatch_nt<6>(a, p, f, s);
+}
+
+template <int NT, int W>
+hipError_t pair_fused_launch(const FxArgs& a0, const FxArgs& a1, int blocks, const FuseArgs& f,
+                             hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_pair_fused_kernel<NT, W, 8>), lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((px_pair_fused_kernel<NT, W, 8>), dim3(blocks), dim3(kWave * (W + 1)),
+                     kStreamLds, s, a0, a1, f);
+  return hipGetLastError();
+}
+
+template <int W>
+hipError_t pair_fused_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks,
+                                  const FuseArgs& f, hipStream_t s) {
+  switch (token_blocks(a0.b)) {
+    case 1: return pair_fused_launch<1, W>(a0, a1, blocks, f, s);
+    case 2: return pair_fused_launch<2, W>(a0, a1, blocks, f, s);
+    case 4: return pair_fused_launch<4, W>(a0, a1, blocks, f, s);
+    default: return pair_fused_launch<8, W>(a0, a1, blocks, f, s);
+  }
+}
+
+hipError_t pair_fused_dispatch(const FxArgs& a0, const FxArgs& a1, const GroupPlan& g, int blocks,
+                               const FuseArgs& f, hipStream_t s) {
+  if (!g.stream || g.hold != 2) return hipErrorInvalidValue;  // not planned
+  if (g.waves == 6) return pair_fused_dispatch_nt<6>(a0, a1, blocks, f, s);
+  if (g.waves == 7) return pair_fused_dispatch_nt<7>(a0, a1, blocks, f, s);
+  return hipErrorInvalidValue;
+}
+
 template <int W, int H>
 hipError_t group_dispatch_nt(const FxArgs& a0, const FxArgs& a1, int blocks0, int blocks,
                              size_t lds, hipStream_t s) {
@@ -1623,6 +1972,44 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
   f32x4_t* part = reinterpret_cast<f32x4_t*>(a.partials);
   f32x4_t* up_part = reinterpret_cast<f32x4_t*>(reinterpret_cast<char*>(a.partials) +
                                                 a.down_part_bytes);
+  const size_t gu_bytes = proj_partial_bytes(gate_up, b, 2 * a.I, true);
+  const size_t dn_bytes = proj_partial_bytes(down, b, a.H, true);
+  const size_t up_bytes = proj_partial_bytes(up, b, a.H, true);
+  if (a.counters && gate_up.stream && gate_up.waves == 6 && g.stream && gu_bytes <= 0x7fffffff &&
+      dn_bytes <= 0x7fffffff && up_bytes <= 0x7fffffff) {
+    // Two launches: gate/up forming h (and y beside it), then the down and
+    // up projections forming rs and out -- the same sums and roundings as
+    // the four launches below.
+    FxArgs gu{a.w_gate, a.w_upw, a.I, 2 * a.I, a.H, a.x, b, gate_up.k_per_split,
+              gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr, a.tiled};
+    FuseArgs f1{};
+    f1.counters = a.counters;
+    f1.out = a.h;
+    f1.splits0 = f1.splits1 = (a.H + gate_up.k_per_split - 1) / gate_up.k_per_split;
+    f1.bytes0 = f1.bytes1 = (uint32_t)gu_bytes;
+    f1.lat = a.lat;
+    f1.gamma = a.gamma;
+    f1.y = a.y;
+    f1.tp = a.tp;
+    f1.L = a.L;
+    f1.eps = a.eps;
+    hipError_t e = gateup_fused_dispatch(gu, gate_up, f1, s);
+    if (e != hipSuccess) return e;
+    FxArgs dn{a.w_down, nullptr, a.H, a.H, a.I, a.h, b, down.k_per_split, g.bps0, down.pitch,
+              part, nullptr, nullptr, a.tiled};
+    FxArgs upa{a.w_up, nullptr, a.H, a.H, a.L, a.y, b, up.k_per_split, g.bps1, up.pitch,
+               up_part, nullptr, nullptr, a.tiled};
+    FuseArgs f2{};
+    f2.counters = a.counters + a.I / 16;
+    f2.out = a.out;
+    f2.rs = a.rs;
+    f2.splits0 = (a.I + down.k_per_split - 1) / down.k_per_split;
+    f2.splits1 = (a.L + up.k_per_split - 1) / up.k_per_split;
+    f2.bytes0 = (uint32_t)dn_bytes;
+    f2.bytes1 = (uint32_t)up_bytes;
+    const int g0 = g.bps0 * down.splits, g1 = g.bps1 * up.splits;
+    return pair_fused_dispatch(dn, upa, g, g0 > g1 ? g0 : g1, f2, s);
+  }
   // 1. gate/up partials
   FxArgs gu{a.w_gate, a.w_upw, a.I, 2 * a.I, a.H, a.x, b, gate_up.k_per_split,
             gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr, a.tiled};

@@ -248,9 +248,12 @@ int moetail_projection_partials(int kind, const uint16_t* w0, const uint16_t* w1
  *     rs  = moetail_shared_expert(x)                       (as that call)
  *     out = moetail_combine_norm_upproj(latent_partials, rs) (as that call)
  * with the hidden width H as the up projection's output width N.  The
- * results are the same bits as those two calls in that order; the work is
- * four launches instead of seven: gate/up; {h, y}; {down, up} projections
- * as one grid; {rs, out}.
+ * results are the same bits as those two calls in that order.  With the
+ * library's own (streamed) plans the work is two launches instead of seven:
+ * gate/up forming h in the launch, beside y; then the down and up
+ * projections as one grid forming rs and out in the launch.  (With plan
+ * overrides that select other kernels: four launches, gate/up; {h, y};
+ * {down, up}; {rs, out}.)
  *
  *   latent_partials [tp][b][L], gamma [L], w_up [H][L]: as in
  *                   moetail_combine_norm_upproj (N = H).
@@ -262,7 +265,11 @@ int moetail_projection_partials(int kind, const uint16_t* w0, const uint16_t* w1
  *   w_layout        MOETAIL_W_ROWS or MOETAIL_W_TILED: the layout of all four
  *                   weights.
  *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_TAIL, b, L,
- *                   H, I) bytes, 256-byte aligned.
+ *                   H, I) bytes, 256-byte aligned, ZERO BEFORE ITS FIRST USE:
+ *                   it starts with the output-tile counters of the launches
+ *                   that form their own split sums, which every call leaves
+ *                   at zero.  A workspace used by another operation in
+ *                   between must be zeroed again.
  *   Limits: those of the two calls: b <= 128, 1 <= tp <= 32, L % 32 == 0,
  *   L <= 8192, H % 64 == 0, I % 64 == 0, H, I <= MOETAIL_MAX_GEMM_K.
  */
@@ -317,8 +324,10 @@ int moetail_decode_tail(const uint16_t* rows, int64_t rows_per_rank,
  * MOETAIL_EWORKSPACE and enqueues nothing; at L = 3584, H = 7168,
  * I = 6144 every b <= 64 fits (18.7 MiB at b = 64).  Every call on a GPU
  * shares that GPU's scratch: calls that overlap on one GPU (other streams,
- * other host threads) race and must not be issued; nothing in the scratch
- * needs to start at zero.  The first call on a device looks the scratch's
+ * other host threads) race and must not be issued.  The scratch starts
+ * with the tail's output-tile counters, which must be zero when a call
+ * starts: a static array is zero when the library loads, and every call
+ * leaves them at zero.  The first call on a device looks the scratch's
  * address up (make it before any graph capture).
  */
 #define MOETAIL_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)

@@ -12,10 +12,11 @@ A step is one pass of the whole tail at b=64 tokens, P=3584:
   3. the rank-order combine of the 8 partials, RMSNorm, and the 3584 -> 7168
      up projection plus rs -> out [64, 7168] (moetail_combine_norm_upproj).
 
-The step is one moetail_decode_tail call (five launches); --tail fused runs
-it as moetail_finalize then moetail_tail (the same five launches), --tail
-calls as moetail_finalize and the tail's two entry points (eight launches):
-the same bits every way.
+The step is one moetail_decode_tail call (three launches: the finalize, the
+gate/up projection forming h with y beside it, the down and up projections
+forming rs and out); --tail fused runs it as moetail_finalize then
+moetail_tail (the same three launches), --tail calls as moetail_finalize and
+the tail's two entry points (eight launches): the same bits every way.
 
 The timed steps replay one HIP graph of G steps on one stream, G the
 largest divisor of the step count up to 40 (a replay boundary costs about
@@ -26,9 +27,10 @@ on a side stream beside the shared expert: measured slower, the cross-stream
 fork and join inside the graph cost more than the overlap gains.)  Inputs
 are resident in HBM before the timed region starts.
 
-The line's roofline object is the step's dominant kernel, the gate/up
-projection's split-K stage, timed alone with HIP events through
-moetail_projection_partials; every entry point's time and fraction, the
+The line's roofline object is the step's dominant kernel, its gate/up launch
+(the gate/up projection forming h, the latent norm's y beside it), timed
+alone with HIP events through moetail_gate_up; every entry point's time and
+fraction (the gate/up projection's split-K stage alone among them), the
 per-config kernels, the targets, a same-size device copy and the CPU
 oracle's rate (on all of this process's host threads and on one) ride along.
 Rank 0 prints one JSON line (progress goes to stderr).
@@ -60,15 +62,15 @@ def graph_steps(steps: int) -> int:
     return max(g for g in range(1, min(steps, MAX_GRAPH_STEPS) + 1) if steps % g == 0)
 
 
-# HBM bytes of one launch of the dominant kernel -- the gate/up projection's
-# split-K stage at b=64 -- from two rocprofv3 --pmc passes over
+# HBM bytes of one launch of the dominant kernel -- the step's gate/up launch
+# at b=64 (moetail_gate_up with y) -- from two rocprofv3 --pmc passes over
 # `bench.py --counters` (FETCH_SIZE, then WRITE_SIZE, per dispatch, that
-# kernel's dispatches averaged), scaled by what each reads for the
-# calibration kernel (256 MiB in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE
-# x 1.0).  They hold for the kernel sources with this digest only (None:
-# not taken for these sources).
-TRAFFIC = dict(source_digest="eb3293bfc1493399", fetch_bytes=88372 * 2 * 1024,
-               write_bytes=6144 * 1024)
+# call's dispatches averaged), scaled by what each reads for the calibration
+# kernel (256 MiB in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
+# They hold for the kernel sources with this digest only (None: not taken
+# for these sources).
+TRAFFIC = dict(source_digest="af15f922114ad0bf", fetch_bytes=93292 * 2 * 1024,
+               write_bytes=7420 * 1024)
 
 
 def kernel_source_digest():
@@ -95,8 +97,12 @@ def algorithmic_bytes():
     # the gate/up projection's split-K stage: its two weight matrices and x
     # (its FP32 partials are an artifact of the split, not counted)
     gate_up = 2 * I * H * 2 + B * H * 2
+    # the step's gate/up launch (moetail_gate_up with y): the stage's bytes,
+    # h out, and the latent norm's partials and gamma in, y out
+    gate_up_h = gate_up + B * I * 2 + TP * B * P * 2 + P * 2 + B * P * 2
     return dict(finalize=fin, shared_expert=shared, combine_norm_upproj=upproj,
-                tail=shared + upproj - B * H * 2 * 2, gate_up_stage=gate_up)
+                tail=shared + upproj - B * H * 2 * 2, gate_up_stage=gate_up,
+                gate_up_h=gate_up_h)
 
 
 def main():
@@ -279,24 +285,35 @@ def main():
         mt.moetail_projection_partials(mt.PROJ_GATEUP, d["wg"], d["wu"], d["x"], gu_part,
                                        w_layout=lay)
 
+    # The step's dominant kernel: its gate/up launch (h formed in the launch,
+    # y beside it), as its own call.
+    gu_ws = mt.new_workspace(mt.OP_GATE_UP, B, H, I)
+    gu_h = torch.empty((B, I), dtype=torch.int16, device="cuda")
+    gu_y = torch.empty((B, P), dtype=torch.int16, device="cuda")
+
+    def gate_up_h(d):
+        mt.moetail_gate_up(d["x"], d["wg"], d["wu"], gu_h, d["lat"], d["lgamma"], 1e-6, gu_y,
+                           workspace=gu_ws, w_layout=lay)
+
     per_call = {n: time_calls(f) for n, f in
                 (("finalize", finalize), ("shared_expert", shared),
                  ("combine_norm_upproj", upproj), ("tail", tail),
-                 ("gate_up_stage", gate_up_stage))}
+                 ("gate_up_stage", gate_up_stage), ("gate_up_h", gate_up_h))}
     algo = algorithmic_bytes()
     entry = {n: dict(us=round(per_call[n], 2), bytes=algo[n],
                      GBps=round(algo[n] / per_call[n] / 1e3, 1),
                      frac=round(algo[n] / per_call[n] / 1e3 / HBM_PEAK_GBPS, 4))
              for n in per_call}
-    dom = "gate_up_stage"
+    dom = "gate_up_h"
     traffic = traffic_bytes = None
     if TRAFFIC["source_digest"] and kernel_source_digest() == TRAFFIC["source_digest"]:
         traffic_bytes = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
         traffic = round(traffic_bytes / per_call[dom] / 1e3, 1)
     roofline = dict(bound="hbm",
-                    kernel="px_stream_kernel<4, 6, 8, 1>: the gate/up projection's split-K stage "
-                           "at b=64 (2 x 6144 x 7168 BF16 weights and x in, FP32 partials out), "
-                           "one launch (moetail_projection_partials)",
+                    kernel="px_gateup_fused_kernel<4, 6, 8>: the decode step's gate/up launch at "
+                           "b=64 (2 x 6144 x 7168 BF16 weights and x in, h formed in the launch; "
+                           "the latent norm's 8 x 64 x 3584 partials in, y out, beside it), one "
+                           "launch (moetail_gate_up)",
                     achieved=entry[dom]["GBps"], peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=entry[dom]["frac"], traffic=traffic, traffic_bytes=traffic_bytes,
                     algorithmic_bytes=algo[dom], us_per_launch=entry[dom]["us"])
@@ -505,6 +522,12 @@ def counter_workloads(sets, step, log, lay, reps=2):
     for _ in range(reps):
         mt.moetail_projection_partials(mt.PROJ_GATEUP, base["wg"], base["wu"], base["x"], gu_part,
                                        w_layout=lay)
+    gws = mt.new_workspace(mt.OP_GATE_UP, B, H, I)
+    gh = torch.empty((B, I), dtype=torch.int16, device="cuda")
+    gy = torch.empty((B, P), dtype=torch.int16, device="cuda")
+    for _ in range(reps):
+        mt.moetail_gate_up(base["x"], base["wg"], base["wu"], gh, base["lat"], base["lgamma"],
+                           1e-6, gy, workspace=gws, w_layout=lay)
     part = torch.empty((TP, B, P), dtype=torch.int16, device="cuda")
     out = torch.empty((B, P), dtype=torch.int16, device="cuda")
     for _ in range(reps):
@@ -544,7 +567,7 @@ def counter_workloads(sets, step, log, lay, reps=2):
     for _ in range(2):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log("counters: gate/up stage b=64, finalize+combine b=64, expert TP b=128, "
+    log("counters: gate/up stage b=64, gate/up + y b=64, finalize+combine b=64, expert TP b=128, "
         "combine+norm+upproj b=32, shared expert b=32 and b=128, calibration 2 x neg over "
         "256 MiB in, 256 MiB out")
 

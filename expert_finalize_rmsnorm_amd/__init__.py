@@ -25,6 +25,7 @@ F32, BF16 = 0, 1
 NORM_GAIN_AFTER, NORM_GAIN_FIRST, NO_NORM = 0, 1, 2  # moetail_finalize norm modes
 OP_FINALIZE, OP_TP_FINALIZE, OP_COMBINE_NORM_UPPROJ, OP_SHARED_EXPERT, OP_TAIL = 0, 1, 2, 3, 4
 OP_PROJECTION = 5
+OP_GATE_UP = 6
 W_ROWS, W_TILED = 0, 1  # weight layouts of the projections
 
 PROJ_UPPROJ, PROJ_GATEUP, PROJ_DOWN = 0, 1, 2  # projection kinds for set_projection_tuning
@@ -32,7 +33,7 @@ PROJ_UPPROJ, PROJ_GATEUP, PROJ_DOWN = 0, 1, 2  # projection kinds for set_projec
 _CALLS = ("moetail_finalize", "moetail_tp_finalize", "moetail_combine_norm_upproj",
           "moetail_shared_expert", "moetail_tail", "moetail_decode_tail", "moetail_pack_weights",
           "moetail_set_projection_tuning", "moetail_decode_tail_noalloc",
-          "moetail_projection_partials")
+          "moetail_projection_partials", "moetail_gate_up")
 ENTRY_POINTS = _CALLS + ("moetail_workspace_bytes", "moetail_status_string",
                          "moetail_plan_cache_stats", "moetail_set_tp_wait_limit")
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.moetail_set_tp_wait_limit.restype = None
         L.moetail_decode_tail_noalloc.argtypes = L.moetail_decode_tail.argtypes[:-3] + [P]
         L.moetail_projection_partials.argtypes = [I32, P, P, I32, I32, P, I32, I32, P, SZ, P]
+        L.moetail_gate_up.argtypes = [P, I32, I32, P, P, I32, P, P, I32, P, F, I32, P, I32, P, SZ,
+                                      P]
         L.moetail_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
         L.moetail_workspace_bytes.restype = SZ
         L.moetail_status_string.argtypes = [I32]
@@ -303,6 +306,40 @@ def moetail_shared_expert(x, w_gate, w_up, w_down, rs, h=None, workspace=None, s
                                      _ptr(h), _ptr(rs), int(w_layout), ws, wsb,
                                      _stream(stream, dev))
     _check(st, "moetail_shared_expert")
+
+
+def moetail_gate_up(x, w_gate, w_up, h, latent_partials=None, gamma=None, eps=1e-6, normed=None,
+                    workspace=None, stream=None, w_layout=W_ROWS):
+    """x [b, H], w_gate/w_up [I, H] (row-major, or pack_weights copies with
+    w_layout=W_TILED); writes h [b, I] in one launch, and with
+    latent_partials [tp, b, L] and gamma [L] also normed [b, L] (the latent
+    combine + RMSNorm) in the same launch.  workspace: at least
+    workspace_bytes(OP_GATE_UP, b, H, I) bytes, zero before its first use
+    (new_workspace)."""
+    if x.dim() != 2 or w_gate.dim() != 2:
+        raise ValueError("x must be [b, H] and w_gate [I, H]")
+    b, H = x.shape
+    I = w_gate.shape[0]
+    _expect(x, "x", (b, H))
+    for t, n in ((w_gate, "w_gate"), (w_up, "w_up")):
+        _expect(t, n, (I, H))
+    _expect(h, "h", (b, I))
+    tp = L = 0
+    if latent_partials is not None:
+        if latent_partials.dim() != 3:
+            raise ValueError("latent_partials must be [tp, b, L]")
+        tp, _, L = latent_partials.shape
+        _expect(latent_partials, "latent_partials", (tp, b, L))
+        _expect(gamma, "gamma", (L,))
+        _expect(normed, "normed", (b, L))
+    elif normed is not None or gamma is not None:
+        raise ValueError("gamma and normed go with latent_partials")
+    dev = _same_device(x, w_gate, w_up, h, latent_partials, gamma, normed, workspace)
+    ws, wsb = _ws(workspace)
+    st = lib().moetail_gate_up(_ptr(x), b, H, _ptr(w_gate), _ptr(w_up), I, _ptr(h),
+                               _ptr(latent_partials), tp, _ptr(gamma), float(eps), L,
+                               _ptr(normed), int(w_layout), ws, wsb, _stream(stream, dev))
+    _check(st, "moetail_gate_up")
 
 
 def moetail_projection_partials(kind, w0, w1, x, partials, stream=None, w_layout=W_ROWS):

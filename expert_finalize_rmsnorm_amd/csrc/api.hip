@@ -213,6 +213,19 @@ UpprojLayout upproj_plan(int b, int L, int N) {
 SharedLayout shared_plan(int b, int H, int I) {
   return plans_for(MOETAIL_OP_SHARED_EXPERT, b, H, I, 0).sh;
 }
+// moetail_gate_up: the shared expert's gate/up plan (the same sums); the
+// h tiles' counters at offset 0, then the partials.
+struct GateUpLayout {
+  ProjPlan plan;
+  size_t counter_bytes, part_bytes;
+};
+GateUpLayout gate_up_plan(int b, int H, int I) {
+  GateUpLayout l;
+  l.plan = shared_plan(b, H, I).gate_up;
+  l.counter_bytes = round_up(sizeof(unsigned) * (size_t)(I / 16), 256);
+  l.part_bytes = round_up(proj_partial_bytes(l.plan, b, 2 * I, true), 256);
+  return l;
+}
 TailLayout tail_plan(int b, int L, int H, int I) {
   return plans_for(MOETAIL_OP_TAIL, b, L, H, I).tail;
 }
@@ -388,6 +401,34 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
   return hip_status(launch_tail(a, lay.gate_up, lay.down, lay.up, lay.group, stream));
 }
 
+int moetail_gate_up(const uint16_t* x, int b, int H, const uint16_t* w_gate,
+                    const uint16_t* w_upw, int I, uint16_t* h,
+                    const uint16_t* latent_partials, int tp, const uint16_t* gamma, float eps,
+                    int L, uint16_t* normed, int w_layout, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (b == 0) return MOETAIL_OK;
+  if (b < 0 || H <= 0 || I <= 0 || !layout_ok(w_layout)) return MOETAIL_EINVAL;
+  if (!a16(x) || !a16(w_gate) || !a16(w_upw) || !a16(h)) return MOETAIL_EINVAL;
+  if (H % 64 || I % 64 || H > MOETAIL_MAX_GEMM_K || I > MOETAIL_MAX_GEMM_K ||
+      b > MOETAIL_MAX_GEMM_TOKENS)
+    return MOETAIL_EUNSUPPORTED;
+  if (latent_partials) {
+    if (tp <= 0 || L <= 0 || !(eps >= 0.0f) || eps == __builtin_inff()) return MOETAIL_EINVAL;
+    if (!a16(latent_partials) || !a16(gamma) || !a16(normed)) return MOETAIL_EINVAL;
+    if (L % 32 || L > MOETAIL_MAX_WIDTH || tp > MOETAIL_MAX_TP) return MOETAIL_EUNSUPPORTED;
+  }
+  const GateUpLayout lay = gate_up_plan(b, H, I);
+  if (lay.plan.splits == 0) return MOETAIL_EUNSUPPORTED;
+  const size_t need = lay.counter_bytes + lay.part_bytes;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
+    return MOETAIL_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(launch_gate_up_h(w_gate, w_upw, w_layout == MOETAIL_W_TILED, I, H, x, b, h,
+                                     lay.plan, reinterpret_cast<float*>(ws + lay.counter_bytes),
+                                     reinterpret_cast<unsigned*>(ws), latent_partials, tp, gamma,
+                                     eps, L, normed, stream));
+}
+
 int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
                          hipStream_t stream) {
   if (n == 0) return MOETAIL_OK;
@@ -522,6 +563,13 @@ size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2) {
         return 0;
       const TailLayout l = tail_plan(b, dim0, dim1, dim2);
       return tail_ok(l) ? l.counter_bytes + l.h_bytes + l.y_bytes + l.part_bytes : 0;
+    }
+    case MOETAIL_OP_GATE_UP: {
+      if (dim0 <= 0 || dim1 <= 0 || dim0 % 64 || dim1 % 64 || dim0 > MOETAIL_MAX_GEMM_K ||
+          dim1 > MOETAIL_MAX_GEMM_K)
+        return 0;
+      const GateUpLayout l = gate_up_plan(b, dim0, dim1);
+      return l.plan.splits ? l.counter_bytes + l.part_bytes : 0;
     }
     case MOETAIL_OP_PROJECTION: {
       if (!projection_dims_ok(dim2, b, dim0, dim1)) return 0;

@@ -142,6 +142,14 @@ hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint1
                          const ProjPlan& plan, float* partials,
                          hipStream_t stream);
 
+// The gate/up projection forming h in its own launch (counters: I/16 words,
+// zero between calls), with the latent norm's y beside it when lat is set;
+// other plans: the separate launches.
+hipError_t launch_gate_up_h(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
+                            const uint16_t* X, int b, uint16_t* h, const ProjPlan& plan,
+                            float* partials, unsigned* counters, const uint16_t* lat, int tp,
+                            const uint16_t* gamma, float eps, int L, uint16_t* y,
+                            hipStream_t stream);
 // h[b][I] = bf16(silu(bf16(Wg . x)) * bf16(Wu . x)), -0 as +0.
 hipError_t launch_gate_up(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
                           const uint16_t* X, int b, uint16_t* h,

@@ -1965,6 +1965,49 @@ GroupPlan plan_group(int b, const ProjPlan& p0, int rows0, const ProjPlan& p1, i
   return best;  // waves == 0: the CUs cannot hold both grids
 }
 
+// The gate/up launch that forms h itself (and y beside it when lat is
+// given): the fused tail's first launch and moetail_gate_up.
+hipError_t gate_up_fused(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
+                         const uint16_t* X, int b, uint16_t* h, const ProjPlan& plan,
+                         f32x4_t* part, size_t part_bytes, unsigned* counters,
+                         const uint16_t* lat, int tp, const uint16_t* gamma, float eps, int L,
+                         uint16_t* y, hipStream_t s) {
+  FxArgs gu{Wg, Wu, I, 2 * I, H, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch, part,
+            nullptr, nullptr, tiled};
+  FuseArgs f{};
+  f.counters = counters;
+  f.out = h;
+  f.splits0 = f.splits1 = (H + plan.k_per_split - 1) / plan.k_per_split;
+  f.bytes0 = f.bytes1 = (uint32_t)part_bytes;
+  f.lat = lat;
+  f.gamma = gamma;
+  f.y = y;
+  f.tp = tp;
+  f.L = L;
+  f.eps = eps;
+  return gateup_fused_dispatch(gu, plan, f, s);
+}
+
+bool gate_up_fusable(int b, const ProjPlan& plan, int I) {
+  return plan.stream && plan.waves == 6 && proj_partial_bytes(plan, b, 2 * I, true) <= 0x7fffffff;
+}
+
+hipError_t launch_gate_up_h(const uint16_t* Wg, const uint16_t* Wu, int tiled, int I, int H,
+                            const uint16_t* X, int b, uint16_t* h, const ProjPlan& plan,
+                            float* partials, unsigned* counters, const uint16_t* lat, int tp,
+                            const uint16_t* gamma, float eps, int L, uint16_t* y,
+                            hipStream_t s) {
+  if (counters && gate_up_fusable(b, plan, I))
+    return gate_up_fused(Wg, Wu, tiled, I, H, X, b, h, plan,
+                         reinterpret_cast<f32x4_t*>(partials),
+                         proj_partial_bytes(plan, b, 2 * I, true), counters, lat, tp, gamma, eps,
+                         L, y, s);
+  // (plans the fused kernel does not take: the separate launches, the same bits)
+  hipError_t e = launch_gate_up(Wg, Wu, tiled, I, H, X, b, h, plan, partials, s);
+  if (e == hipSuccess && lat) e = launch_latent_norm(lat, tp, b, L, gamma, eps, y, s);
+  return e;
+}
+
 hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPlan& down,
                        const ProjPlan& up, const GroupPlan& g, hipStream_t s) {
   const int b = a.b;
@@ -1980,20 +2023,8 @@ hipError_t launch_tail(const TailArgs& a, const ProjPlan& gate_up, const ProjPla
     // Two launches: gate/up forming h (and y beside it), then the down and
     // up projections forming rs and out -- the same sums and roundings as
     // the four launches below.
-    FxArgs gu{a.w_gate, a.w_upw, a.I, 2 * a.I, a.H, a.x, b, gate_up.k_per_split,
-              gate_up.blocks_per_slice, gate_up.pitch, part, nullptr, nullptr, a.tiled};
-    FuseArgs f1{};
-    f1.counters = a.counters;
-    f1.out = a.h;
-    f1.splits0 = f1.splits1 = (a.H + gate_up.k_per_split - 1) / gate_up.k_per_split;
-    f1.bytes0 = f1.bytes1 = (uint32_t)gu_bytes;
-    f1.lat = a.lat;
-    f1.gamma = a.gamma;
-    f1.y = a.y;
-    f1.tp = a.tp;
-    f1.L = a.L;
-    f1.eps = a.eps;
-    hipError_t e = gateup_fused_dispatch(gu, gate_up, f1, s);
+    hipError_t e = gate_up_fused(a.w_gate, a.w_upw, a.tiled, a.I, a.H, a.x, b, a.h, gate_up, part,
+                                 gu_bytes, a.counters, a.lat, a.tp, a.gamma, a.eps, a.L, a.y, s);
     if (e != hipSuccess) return e;
     FxArgs dn{a.w_down, nullptr, a.H, a.H, a.I, a.h, b, down.k_per_split, g.bps0, down.pitch,
               part, nullptr, nullptr, a.tiled};

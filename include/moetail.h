@@ -68,6 +68,7 @@ extern "C" {
 #define MOETAIL_OP_SHARED_EXPERT 3
 #define MOETAIL_OP_TAIL 4
 #define MOETAIL_OP_PROJECTION 5
+#define MOETAIL_OP_GATE_UP 6
 
 /* Projection kinds of moetail_set_projection_tuning. */
 #define MOETAIL_PROJ_UPPROJ 0 /* the up projection (moetail_combine_norm_upproj, the tail's) */
@@ -242,6 +243,37 @@ int moetail_projection_partials(int kind, const uint16_t* w0, const uint16_t* w1
                                 size_t partial_bytes, hipStream_t stream);
 
 /*
+ * The shared expert's gate/up projection and its activation in one launch
+ * ([shared] module docstring: h = bf16(SiLU(x W_g^T) * (x W_u^T))), with,
+ * when latent_partials is given, the latent combine + RMSNorm y of
+ * moetail_combine_norm_upproj formed by the same launch beside it: the first
+ * launch of moetail_tail, as a call of its own.  The K-split sums are formed
+ * in the launch (per-tile counters in the workspace; the wave completing a
+ * tile adds its splits in split order, the bits of the separate sum).
+ *
+ *   x [b][H], w_gate, w_upw [I][H], w_layout: as in moetail_shared_expert.
+ *   h               [b][I] BF16 written: the bits moetail_shared_expert
+ *                   writes to its h.
+ *   latent_partials [tp][b][L], gamma [L], eps: as in
+ *                   moetail_combine_norm_upproj; normed [b][L] BF16 written
+ *                   (its normed bits).  latent_partials NULL: no y (tp,
+ *                   gamma, eps, L and normed are not read).
+ *   workspace       at least moetail_workspace_bytes(MOETAIL_OP_GATE_UP, b,
+ *                   H, I) bytes, 256-byte aligned, ZERO BEFORE ITS FIRST USE
+ *                   (it starts with the h tiles' counters; every call leaves
+ *                   them at zero).
+ *   Limits: those of moetail_shared_expert, and with y those of
+ *   moetail_combine_norm_upproj (tp <= 32, L % 32 == 0, L <= 8192).  With
+ *   plan overrides that select other kernels the work is the separate
+ *   launches (the same bits).
+ */
+int moetail_gate_up(const uint16_t* x, int b, int H, const uint16_t* w_gate,
+                    const uint16_t* w_upw, int I, uint16_t* h,
+                    const uint16_t* latent_partials, int tp, const uint16_t* gamma,
+                    float eps, int L, uint16_t* normed, int w_layout, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The decode tail after the finalize in one call ([tail_runtime] module
  * docstring: the latent combine, RMSNorm and K-split up projection with the
  * shared expert's reduce-scatter partial added; [shared] for that partial):
@@ -373,6 +405,7 @@ int moetail_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* packed,
  *   MOETAIL_OP_SHARED_EXPERT:       dim0 = H, dim1 = I
  *   MOETAIL_OP_TAIL:                dim0 = L, dim1 = H, dim2 = I
  *   MOETAIL_OP_PROJECTION:          dim0 = N, dim1 = K, dim2 = kind
+ *   MOETAIL_OP_GATE_UP:             dim0 = H, dim1 = I
  * Returns 0 for an unknown op or out-of-range sizes.
  */
 size_t moetail_workspace_bytes(int op, int b, int dim0, int dim1, int dim2);

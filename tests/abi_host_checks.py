@@ -170,6 +170,50 @@ def test_shared_validation():
     assert _sh(lay=5) == mt.EINVAL
 
 
+def _gu(ws=A, wsb=1 << 30, **kw):
+    a = dict(x=A, b=64, H=7168, wg=A, wu=A, I=6144, h=A, lat=A, tp=8, g=A, eps=1e-6, L=3584,
+             y=A, lay=mt.W_TILED)
+    a.update(kw)
+    return mt.lib().moetail_gate_up(a["x"], a["b"], a["H"], a["wg"], a["wu"], a["I"], a["h"],
+                                    a["lat"], a["tp"], a["g"], a["eps"], a["L"], a["y"],
+                                    a["lay"], ws, wsb, None)
+
+
+def test_gate_up_validation():
+    assert _gu(b=0) == mt.OK
+    assert _gu(b=0, x=None, ws=None, wsb=0) == mt.OK  # b == 0 before any check
+    assert _gu(x=None) == mt.EINVAL
+    assert _gu(h=None) == mt.EINVAL
+    assert _gu(wu=A + 2) == mt.EINVAL
+    assert _gu(lay=3) == mt.EINVAL
+    assert _gu(H=7160) == mt.EUNSUPPORTED
+    assert _gu(I=6100) == mt.EUNSUPPORTED
+    assert _gu(b=129) == mt.EUNSUPPORTED
+    # y's arguments are checked only with latent partials
+    assert _gu(g=None) == mt.EINVAL
+    assert _gu(y=A + 8) == mt.EINVAL
+    assert _gu(eps=-1.0) == mt.EINVAL
+    assert _gu(tp=0) == mt.EINVAL
+    assert _gu(L=3600) == mt.EUNSUPPORTED
+    assert _gu(tp=33) == mt.EUNSUPPORTED
+    assert _gu(lat=None, g=None, y=None, tp=0, L=0, eps=float("nan"), ws=None,
+               wsb=0) == mt.EWORKSPACE
+    need = mt.workspace_bytes(mt.OP_GATE_UP, 64, 7168, 6144)
+    assert _gu(wsb=need - 1) == mt.EWORKSPACE
+    assert _gu(ws=A + 16) == mt.EWORKSPACE  # 256-byte aligned
+
+
+@pytest.mark.parametrize("b", [1, 32, 64, 128])
+def test_gate_up_workspace(b):
+    """The h tiles' counters (I/16 words, rounded to 256 bytes), then the
+    gate/up partials of the shared expert's plan."""
+    gu = mt.workspace_bytes(mt.OP_GATE_UP, b, 7168, 6144)
+    part = mt.workspace_bytes(mt.OP_PROJECTION, b, 12288, 7168, mt.PROJ_GATEUP)
+    assert gu == (6144 // 16 * 4 + 255) // 256 * 256 + part
+    assert mt.workspace_bytes(mt.OP_GATE_UP, b, 7160, 6144) == 0
+    assert mt.workspace_bytes(mt.OP_GATE_UP, b, 7168, 6100) == 0
+
+
 def _proj(**kw):
     a = dict(kind=mt.PROJ_GATEUP, w0=A, w1=A, N=12288, K=7168, x=A, b=64, lay=mt.W_TILED,
              part=A, pb=1 << 31)

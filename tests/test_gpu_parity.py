@@ -786,6 +786,67 @@ def test_tail_graph_replay():
         assert np.array_equal(host(out), eager[0]) and np.array_equal(host(rs), eager[1])
 
 
+@pytest.mark.parametrize("b,tp,L,H,I,layout", [(64, 8, 3584, 7168, 6144, mt.W_TILED),
+                                               (32, 8, 3584, 7168, 6144, mt.W_ROWS),
+                                               (5, 3, 544, 256, 128, mt.W_ROWS),
+                                               (40, 2, 1024, 512, 192, mt.W_TILED)])
+def test_gate_up_is_the_shared_expert_h_and_the_norm(b, tp, L, H, I, layout):
+    """moetail_gate_up forms h and y in one launch: the bits of
+    moetail_shared_expert's h and moetail_combine_norm_upproj's normed, with
+    and without y, and again on the same workspace (its counters back at
+    zero)."""
+    up = workloads.upproj(b + L + 1, b=b, tp=tp, L=L, N=H)
+    sh = workloads.shared(b + H + 1, b=b, H=H, I=I)
+    lat, gamma = dev(up["lat"]), dev(up["gamma"])
+    x, wg, wu, wd = (dev(sh["x"]), weight(sh["w_gate"], layout), weight(sh["w_up"], layout),
+                     weight(sh["w_down"], layout))
+    h_ref, rs = empty_bf16(b, I), empty_bf16(b, H)
+    mt.moetail_shared_expert(x, wg, wu, wd, rs, h=h_ref,
+                             workspace=mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I),
+                             w_layout=layout)
+    y_ref, out = empty_bf16(b, L), empty_bf16(b, H)
+    mt.moetail_combine_norm_upproj(lat, gamma, up["eps"], weight(up["w_up"], layout), out,
+                                   normed=y_ref,
+                                   workspace=mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L,
+                                                              H, tp), w_layout=layout)
+    ws = mt.new_workspace(mt.OP_GATE_UP, b, H, I)
+    for with_y in (True, False, True):
+        h, y = empty_bf16(b, I), empty_bf16(b, L)
+        if with_y:
+            mt.moetail_gate_up(x, wg, wu, h, lat, gamma, up["eps"], y, workspace=ws,
+                               w_layout=layout)
+            assert np.array_equal(host(y), host(y_ref))
+        else:
+            mt.moetail_gate_up(x, wg, wu, h, workspace=ws, w_layout=layout)
+        assert np.array_equal(host(h), host(h_ref)), with_y
+        assert int(ws[: 4 * (I // 16)].view(torch.int32).abs().sum()) == 0
+
+
+def test_tail_counters_back_to_zero():
+    """The fused tail forms its split sums in its own launches with per-tile
+    counters at the start of the workspace (I/16 h-tile words, then H/16
+    output-tile words), which must be zero when a call starts.  Every call
+    leaves them at zero: back-to-back calls on one workspace, at token counts
+    of different plans, give the bits of calls on fresh workspaces."""
+    L, H, I, tp = 544, 256, 128, 3
+    sizes = (40, 5, 40, 1)
+    ws = torch.zeros(max(mt.workspace_bytes(mt.OP_TAIL, b, L, H, I) for b in sizes),
+                     dtype=torch.uint8, device="cuda")
+    words = I // 16 + H // 16
+    for k, b in enumerate(sizes):
+        up = workloads.upproj(b + k, b=b, tp=tp, L=L, N=H)
+        sh = workloads.shared(b + 7 * k, b=b, H=H, I=I)
+        args = (dev(up["lat"]), dev(up["gamma"]), up["eps"], dev(up["w_up"]), dev(sh["x"]),
+                dev(sh["w_gate"]), dev(sh["w_up"]), dev(sh["w_down"]))
+        out, rs = empty_bf16(b, H), empty_bf16(b, H)
+        mt.moetail_tail(*args, out, rs=rs, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[: 4 * words].view(torch.int32).abs().sum()) == 0, f"b={b}"
+        out2, rs2 = empty_bf16(b, H), empty_bf16(b, H)
+        mt.moetail_tail(*args, out2, rs=rs2, workspace=mt.new_workspace(mt.OP_TAIL, b, L, H, I))
+        assert np.array_equal(host(out), host(out2)) and np.array_equal(host(rs), host(rs2)), b
+
+
 # ------------------------------- finalize without a per-route norm (Kimi) --
 
 def run_plain(inp, wkey="w32", mode="both", gamma=True):

@@ -1302,6 +1302,182 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
   *reinterpret_cast<uint2*>(out + (int64_t)tok * N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
 }
 
+// --------------------------------------- a projection summed in its blocks
+//
+// A linear projection (the up projection, the shared expert's down
+// projection) for up to 16 tokens in one launch: a block holds every K split
+// of its row tiles, one consumer wave per (tile, split) over the plan's K
+// range of that split.  So each wave's FP32 sum is, bit for bit, the split
+// partial the streamed kernel writes (the same MFMAs on the same operands in
+// the same k order).  The producer wave stages each chunk of activations
+// for all of the block's K ranges side by side, one sub-chunk per split.  At
+// the end the waves leave their sums in LDS, and the block adds a tile's
+// splits in split order from +0, adds rs and rounds once: split_reduce_kernel's
+// arithmetic, with no partials in memory, no second launch, and no wait on
+// any other block.
+constexpr int kLocalWaves = 8;  // consumer waves a block: splits x row tiles
+
+struct LocalArgs {
+  const uint16_t* W;        // [N][K] row-major, or the tiled layout
+  const uint16_t* X;        // [b][K]
+  const uint16_t* rs;       // [b][N] or null
+  uint16_t* out;            // [b][N]
+  int N, K, b, tiled;
+  int k_per_split;          // the plan's K range of a split (a multiple of 32)
+};
+
+// Columns of one split's sub-chunk: NT token blocks x kLocalCols fill the
+// chunk with kS sub-chunks; at least 16 pieces of 8 a row, so the piece
+// swizzle (piece ^ row) stays inside the row.
+template <int NT, int kS>
+constexpr int kLocalCols = kStreamCols<NT> / kS;
+template <int NT>
+constexpr int kLocalLds = kRing * kStreamChunkBytes + 256 + kLocalWaves * NT * kWave * 16;
+
+// Chunk x's activations for every split into its ring buffer (not waited
+// for): sub-chunk q holds token rows 0 .. 16 NT - 1 of columns
+// q kr + x kc .. + kc, each row's pieces swizzled by the row as in the
+// streamed kernel.  Columns past the split's range or past K are valid
+// pieces that no wave reads.
+template <int NT, int kS>
+__device__ __forceinline__ void local_issue(const LocalArgs& a, uint16_t* xs, int x) {
+  constexpr int kc = kLocalCols<NT, kS>;
+  constexpr int kSub = 16 * NT * kc;  // elements of a sub-chunk
+  constexpr int kChunkElems = kStreamChunkBytes / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint16_t* buf = xs + (x % kRing) * kChunkElems;
+#pragma unroll
+  for (int j = 0; j < kStreamLoads; ++j) {
+    const int e = j * 512 + lane * 8;
+    const int q = e / kSub;
+    const int rem = e - q * kSub;
+    const int t = rem / kc;
+    const int piece = ((rem - t * kc) >> 3) ^ (t & 15);
+    const int col = min(q * a.k_per_split + x * kc + 8 * piece, a.K - 8);
+    const uint16_t* g = a.X + (int64_t)min(t, a.b - 1) * a.K + col;
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
+  }
+}
+
+template <int NT, int kS, int kPF>
+__global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(LocalArgs a) {
+  static_assert(kLocalWaves % kS == 0 && kLocalCols<NT, kS> >= 128, "sub-chunk shape");
+  constexpr int kT = kLocalWaves / kS;     // row tiles a block
+  constexpr int kc = kLocalCols<NT, kS>;
+  constexpr int kSpc = kc / kKStep;        // k steps of a sub-chunk
+  constexpr int kSub = 16 * NT * kc;
+  constexpr int kChunkElems = kStreamChunkBytes / 2;
+  extern __shared__ uint16_t xs[];
+  int* flags = reinterpret_cast<int*>(xs + kRing * kChunkElems);
+  f32x4_t* sums = reinterpret_cast<f32x4_t*>(xs + kRing * kChunkElems + 128);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lrow = lane & 15;
+  const int kq = lane >> 4;
+  const int pos = xcd_position(blockIdx.x, 0, gridDim.x);
+  const int ntiles = a.N / 16;
+  const int kr = a.k_per_split;
+  const int nchunks = (kr + kc - 1) / kc;  // split 0's range is the longest
+  if (threadIdx.x < 1 + kLocalWaves) flag_set(flags + threadIdx.x, 0);
+  if (wave == kLocalWaves) local_issue<NT, kS>(a, xs, 0);
+  lds_barrier();
+
+  if (wave == kLocalWaves) {
+    // The producer: chunk x once every consumer is past chunk x - kRing.  A
+    // block stages the activations of all its K ranges (half as many bytes
+    // as its weights at 16 tokens), so two chunks stay in flight: chunk x - 1
+    // is published once chunk x's loads are out and x - 1's have landed
+    // (direct loads complete in order: at most chunk x's kStreamLoads left).
+    for (int x = 1; x < nchunks; ++x) {
+      if (x >= kRing) {
+        const int need = x - kRing + 1;
+        for (int it = 0; it < kSpinLimit; ++it) {
+          const int v = lane < kLocalWaves ? flag_get(flags + 1 + lane) : need;
+          if (__ballot(v < need) == 0) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+      }
+      local_issue<NT, kS>(a, xs, x);
+      static_assert(kStreamLoads == 32, "the wait below counts one chunk's loads");
+      asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      if (lane == 0) flag_set(flags, x);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) flag_set(flags, nchunks);
+  } else {
+    const int tau = wave / kS, split = wave - tau * kS;
+    const int tile = pos * kT + tau;
+    const int kb0 = split * kr;
+    const int klen = (tile < ntiles && kb0 < a.K) ? min(kr, a.K - kb0) : 0;
+    const int steps = klen / kKStep;
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (steps == 0) {
+      if (lane == 0) flag_set(flags + 1 + wave, nchunks);
+    } else {
+      const int row0 = tile * 16;
+      const uint16_t* wp = a.tiled ? a.W + (int64_t)row0 * a.K + (int64_t)kb0 * 16 + 8 * lane
+                                   : a.W + (int64_t)(row0 + lrow) * a.K + kb0 + 8 * kq;
+      const int sstride = a.tiled ? 512 : kKStep;
+      uint4 ra[kPF];
+#pragma unroll
+      for (int i = 0; i < kPF; ++i) ra[i] = load16_stream(wp + (int64_t)min(i, steps - 1) * sstride);
+      // operand reads: sub-chunk `split`, token row 16 nt + lrow, piece
+      // (4 step + kq) ^ lrow
+      const int xoff = split * kSub + lrow * kc;
+      for (int q0 = 0; q0 < steps; q0 += kPF) {
+#pragma unroll
+        for (int i = 0; i < kPF; ++i) {
+          const int st = q0 + i;
+          if (st < steps) {
+            const int cx = st / kSpc, ci = st - cx * kSpc;
+            if (ci == 0) wait_filled(flags, cx + 1);
+            const uint16_t* xp =
+                xs + (cx % kRing) * kChunkElems + xoff + (((4 * ci + kq) ^ lrow) << 3);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const uint4 bq = *reinterpret_cast<const uint4*>(xp + 16 * nt * kc);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, ra[i]), __builtin_bit_cast(bf16x8_t, bq), acc[nt],
+                  0, 0, 0);
+            }
+            if (st == steps - 1 || ci == kSpc - 1) {
+              // done with this chunk's buffer (with the range: with all of them)
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              if (lane == 0) flag_set(flags + 1 + wave, st == steps - 1 ? nchunks : cx + 1);
+            }
+            ra[i] = load16_stream(wp + (int64_t)min(st + kPF, steps - 1) * sstride);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sums[(wave * NT + nt) * kWave + lane] = acc[nt];
+  }
+  lds_barrier();
+
+  // Output tile tau's token block nt on wave tau NT + nt: the splits' sums in
+  // split order from +0, + rs, one rounding (-0 as +0).  Accumulator lane
+  // layout: rows 16 tile + 4 (lane / 16) + v, token 16 nt + lane % 16.
+  if (wave < kT * NT) {
+    const int tau = wave / NT, nt = wave - tau * NT;
+    const int tile = pos * kT + tau;
+    const int tok = 16 * nt + lrow;
+    if (tile < ntiles && tok < a.b) {
+      f32x4_t z = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kS; ++s)
+        if (s * kr < a.K) z = z + sums[((tau * kS + s) * NT + nt) * kWave + lane];
+      const int r = tile * 16 + 4 * kq;
+      float o[4] = {z[0], z[1], z[2], z[3]};
+      if (a.rs) add_bf16x4(o, *reinterpret_cast<const uint2*>(a.rs + (int64_t)tok * a.N + r));
+      *reinterpret_cast<uint2*>(a.out + (int64_t)tok * a.N + r) = pack4_pz(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 // Tiled weight layout: fragment (t, s) of a [N][K] matrix -- rows
 // 16 t .. 16 t + 15, columns 32 s .. 32 s + 31 -- is 1 KB at element
 // (t * K/32 + s) * 512, lane l's 8 values (row 16 t + l % 16, columns
@@ -2102,9 +2278,47 @@ hipError_t launch_pack_weights(const uint16_t* w, int64_t n, int k, uint16_t* pa
   return hipGetLastError();
 }
 
+template <int NT, int kS>
+hipError_t local_launch(const LocalArgs& a, hipStream_t s) {
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e =
+      allow_full_lds(reinterpret_cast<const void*>(px_local_kernel<NT, kS, 8>), lds_set);
+  if (e != hipSuccess) return e;
+  constexpr int kT = kLocalWaves / kS;
+  const int blocks = (a.N / 16 + kT - 1) / kT;
+  hipLaunchKernelGGL((px_local_kernel<NT, kS, 8>), dim3(blocks), dim3(kWave * (kLocalWaves + 1)),
+                     kLocalLds<NT>, s, a);
+  return hipGetLastError();
+}
+
+// The streamed plans whose K splits one block holds: one token block, and
+// 4 splits (2 row tiles a block: 224 blocks for 7168 rows) or 8.  A block
+// stages the activations of all its K ranges, half its weight bytes at 16
+// tokens and as many at 32, where the split-K launch stages 0.29 of them:
+// measured at 32 tokens the block-local launch ran 2.2 us (up projection)
+// and 3.9 us (down projection) longer than the split-K launch, more than
+// the sum launch it saves.  Other plans keep the split-K launch and its sum
+// launch.
+bool linear_local(int b, const ProjPlan& p) {
+  return p.stream && p.passes <= 1 && token_blocks(b) == 1 && (p.splits == 4 || p.splits == 8);
+}
+
+hipError_t local_dispatch(const LocalArgs& a, const ProjPlan& p, hipStream_t s) {
+  if (token_blocks(a.b) != 1) return hipErrorInvalidValue;  // not a shape linear_local takes
+  switch (p.splits) {
+    case 4: return local_launch<1, 4>(a, s);
+    case 8: return local_launch<1, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_linear(const uint16_t* W, int tiled, int N, int K, const uint16_t* X, int b,
                          const uint16_t* rs, uint16_t* out, const ProjPlan& plan,
                          float* partials, hipStream_t s) {
+  if (linear_local(b, plan)) {
+    const LocalArgs la{W, X, rs, out, N, K, b, tiled, plan.k_per_split};
+    return local_dispatch(la, plan, s);
+  }
   const bool split = plan.splits > 1 || plan.passes > 1 || plan.stream;  // (streamed: always partials)
   f32x4_t* part = reinterpret_cast<f32x4_t*>(partials);
   FxArgs a{W, nullptr, N, N, K, X, b, plan.k_per_split, plan.blocks_per_slice, plan.pitch,

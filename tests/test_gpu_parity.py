@@ -1038,6 +1038,56 @@ def test_projection_partials_are_the_shared_experts():
     assert np.isfinite(part.cpu().numpy()).all()
 
 
+@pytest.mark.parametrize("b,L,N,layout", [(16, 3584, 7168, mt.W_TILED), (9, 3584, 7168, mt.W_ROWS),
+                                          (1, 3584, 7168, mt.W_TILED), (16, 3616, 7168, mt.W_TILED),
+                                          (5, 128, 256, mt.W_ROWS), (32, 3584, 7168, mt.W_TILED)])
+def test_upproj_block_sums_are_the_split_k_stage(b, L, N, layout):
+    """Up to 16 tokens the up projection adds its K splits inside its blocks
+    (one launch after the norm); above, a split-K launch and a sum launch.
+    Either way its out is, bit for bit, the split-K stage's partials of the
+    same y added in split order from +0, plus rs, rounded once (-0 as +0).
+    L = 3616: 4 splits of 928 columns, the last one shorter; 128 -> 256: 4
+    splits of one k step."""
+    up = workloads.upproj(90 + b, b=b, L=L, N=N, with_rs=True)
+    w = weight(up["w_up"], layout)
+    lat, gamma, rs = dev(up["lat"]), dev(up["gamma"]), dev(up["rs"])
+    out, normed = empty_bf16(b, N), empty_bf16(b, L)
+    ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, L, N, up["tp"])
+    mt.moetail_combine_norm_upproj(lat, gamma, up["eps"], w, out, rs=rs, normed=normed,
+                                   workspace=ws, w_layout=layout)
+    n = mt.workspace_bytes(mt.OP_PROJECTION, b, N, L, mt.PROJ_UPPROJ)
+    part = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    mt.moetail_projection_partials(mt.PROJ_UPPROJ, w, None, normed, part, w_layout=layout)
+    acc = np.zeros((b, N), np.float32)
+    for s_ in partial_sums(part.cpu().numpy(), N, b):
+        acc = acc + s_
+    acc = acc + oracle.f32(up["rs"])
+    acc[acc == 0] = 0.0  # -0 as +0
+    assert np.array_equal(oracle.bf16_round(acc), host(out))
+
+
+@pytest.mark.parametrize("b", [1, 11, 16, 32])
+def test_shared_down_block_sums_are_the_split_k_stage(b):
+    """The shared expert's down projection (summed inside its blocks up to 16
+    tokens): rs is, bit for bit, the split-K stage's partials of the same h
+    added in split order from +0 and rounded once (-0 as +0)."""
+    sh = workloads.shared(95 + b, b=b)
+    wg, wu, wd = (mt.pack_weights(dev(a)) for a in (sh["w_gate"], sh["w_up"], sh["w_down"]))
+    x = dev(sh["x"])
+    H, I = sh["H"], sh["I"]
+    h, rs = empty_bf16(b, I), empty_bf16(b, H)
+    ws = mt.new_workspace(mt.OP_SHARED_EXPERT, b, H, I)
+    mt.moetail_shared_expert(x, wg, wu, wd, rs, h=h, workspace=ws, w_layout=mt.W_TILED)
+    n = mt.workspace_bytes(mt.OP_PROJECTION, b, H, I, mt.PROJ_DOWN)
+    part = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    mt.moetail_projection_partials(mt.PROJ_DOWN, wd, None, h, part, w_layout=mt.W_TILED)
+    acc = np.zeros((b, H), np.float32)
+    for s_ in partial_sums(part.cpu().numpy(), H, b):
+        acc = acc + s_
+    acc[acc == 0] = 0.0  # -0 as +0
+    assert np.array_equal(oracle.bf16_round(acc), host(rs))
+
+
 # ------------------------------------------------- the fused decode tail --
 
 def run_decode_tail(ep, up, sh, mode, wkey="w32", layout=mt.W_TILED):

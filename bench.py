@@ -69,7 +69,7 @@ def graph_steps(steps: int) -> int:
 # kernel (256 MiB in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # They hold for the kernel sources with this digest only (None: not taken
 # for these sources).
-TRAFFIC = dict(source_digest="af15f922114ad0bf", fetch_bytes=93292 * 2 * 1024,
+TRAFFIC = dict(source_digest="876dcbab74c60668", fetch_bytes=93288 * 2 * 1024,
                write_bytes=7420 * 1024)
 
 
@@ -547,12 +547,14 @@ def counter_workloads(sets, step, log, lay, reps=2):
         mt.moetail_tp_finalize(kp, idx, dev(w32), dev(tgamma), 0.0, 1e-6, False, tout,
                                workspace=tws)
     del kp
-    lat = torch.randn((TP, 32, P), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
-    o = torch.empty((32, H), dtype=torch.int16, device="cuda")
-    ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, 32, P, H, TP)
-    for _ in range(reps):
-        mt.moetail_combine_norm_upproj(lat, base["lgamma"], 1e-6, base["w_up"], o, workspace=ws,
-                                       w_layout=lay)
+    for b in (8, 32):  # (b = 8: the block-local kernel, one launch after the norm)
+        lat = torch.randn((TP, b, P), device="cuda", generator=gen).to(torch.bfloat16).view(
+            torch.int16)
+        o = torch.empty((b, H), dtype=torch.int16, device="cuda")
+        ws = mt.new_workspace(mt.OP_COMBINE_NORM_UPPROJ, b, P, H, TP)
+        for _ in range(reps):
+            mt.moetail_combine_norm_upproj(lat, base["lgamma"], 1e-6, base["w_up"], o,
+                                           workspace=ws, w_layout=lay)
     for b in (32, 128):
         x = torch.randn((b, H), device="cuda", generator=gen).to(torch.bfloat16).view(torch.int16)
         rs = torch.empty((b, H), dtype=torch.int16, device="cuda")
@@ -568,8 +570,8 @@ def counter_workloads(sets, step, log, lay, reps=2):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log("counters: gate/up stage b=64, gate/up + y b=64, finalize+combine b=64, expert TP b=128, "
-        "combine+norm+upproj b=32, shared expert b=32 and b=128, calibration 2 x neg over "
-        "256 MiB in, 256 MiB out")
+        "combine+norm+upproj b=8 and b=32, shared expert b=32 and b=128, calibration 2 x neg "
+        "over 256 MiB in, 256 MiB out")
 
 
 def cpu_model():

@@ -271,8 +271,8 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us wall, {gpu_ms * 1e3:.1f} us GPU events")
 
     # Per entry point: a HIP graph of back-to-back calls (rotating the input
-    # sets), HIP events around one replay; the host's launch rate is out of
-    # the measurement.
+    # sets), HIP events around each of 20 replays, the median; the host's
+    # launch rate is out of the measurement.
     def time_calls(fn, reps=20):
         return graph_time(lambda i: fn(sets[i % nsets]), reps)
 
@@ -378,9 +378,11 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def graph_time(fn, reps):
-    """Microseconds per call of fn(i), i = 0..reps-1, from one replay of a
-    HIP graph holding the reps calls (after one untimed replay)."""
+def graph_time(fn, reps, replays=20):
+    """Microseconds per call of fn(i), i = 0..reps-1: a HIP graph holds the
+    reps calls; after one untimed replay, HIP events time `replays` replays
+    one by one, and the median replay is taken."""
+    import statistics
     import torch
     for i in range(min(reps, 4)):
         fn(i)
@@ -391,12 +393,15 @@ def graph_time(fn, reps):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / reps
+    times = []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3 / reps)
+    return statistics.median(times)
 
 
 def config_kernels(base, log, lay):
@@ -647,7 +652,7 @@ def cpu_baseline(host_inputs, log, seconds=(8.0, 10.0)):
 
 def copy_ceiling(nbytes, reps=10):
     """A device-to-device copy of nbytes (read nbytes, write nbytes), HIP
-    events around one replay of a graph of reps copies: the bandwidth a
+    events around replays of a graph of reps copies (the median): the bandwidth a
     plain copy reaches on this GPU, as the practical ceiling beside the
     8 TB/s peak."""
     import torch

@@ -826,28 +826,56 @@ __device__ __forceinline__ void stream_issue(const StreamPhase& ph0, const Strea
   }
 }
 
-// Chunk 0 was issued before the block's first barrier.
+// The producers' LDS flag accesses, each one LDS instruction.  Before any
+// LDS access of a wave with direct global->LDS loads in flight, the
+// compiler waits for all of them (it cannot tell a flag from the ring
+// buffers those loads fill), which would leave one chunk in flight.  The
+// producers order these accesses themselves: a chunk's flag is written
+// after s_waitcnt vmcnt(kStreamLoads), when that chunk's loads have
+// completed (a wave's vector memory operations complete in issue order) and
+// only the next chunk's are still in flight; a read waits for its result
+// in the same statement.
+static_assert(kStreamLoads == 32, "the producers' waits count one chunk's loads");
+__device__ __forceinline__ int producer_flag_get(const int* f) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(v)
+               : "v"((unsigned)(size_t)(lds_ptr_t)const_cast<int*>(f))
+               : "memory");
+  return v;
+}
+__device__ __forceinline__ void producer_flag_set(int* f, int v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"((unsigned)(size_t)(lds_ptr_t)f), "v"(v) : "memory");
+}
+
+// Waits (bounded) until every consumer's flag is at least `need`.
+template <int kW>
+__device__ __forceinline__ void producer_wait(const int* flags, int need) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int* mine = flags + 1 + (lane < kW ? lane : 0);
+  for (int it = 0; it < kSpinLimit; ++it) {
+    const int v = producer_flag_get(mine);
+    if (__ballot(lane < kW && v < need) == 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Chunk 0 was issued before the block's first barrier.  Two chunks stay in
+// flight: chunk x - 1 is published once chunk x's loads are out and x - 1's
+// have landed.  Buffer x % kRing is refilled once every consumer is done
+// with chunk x - kRing.
 template <int NT, int kW, int kPhases>
 __device__ __forceinline__ void stream_producer(const StreamPhase& ph0, const StreamPhase& ph1,
                                                 uint16_t* xs, int* flags, int nchunks) {
   const int lane = threadIdx.x & (kWave - 1);
-  for (int x = 0; x < nchunks; ++x) {
-    if (x >= kRing) {
-      // buffer x % kRing is free once every consumer is done with chunk x - kRing
-      const int need = x - kRing + 1;
-      for (int it = 0; it < kSpinLimit; ++it) {
-        const int v = lane < kW ? flag_get(flags + 1 + lane) : need;
-        if (__ballot(v < need) == 0) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      asm volatile("" ::: "memory");
-    }
-    if (x > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, x);
-    // the chunk has landed in LDS, then it is published (an LDS write
-    // after direct loads waits for them in any case)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0) flag_set(flags, x + 1);
+  for (int x = 1; x < nchunks; ++x) {
+    if (x >= kRing) producer_wait<kW>(flags, x - kRing + 1);
+    stream_issue<NT, kPhases>(ph0, ph1, xs, x);
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+    if (lane == 0) producer_flag_set(flags, x);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0) producer_flag_set(flags, nchunks);
 }
 
 // kPhases (1 or 2) projections in one streamed block: a0's chunks, then
@@ -1305,7 +1333,7 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
 // --------------------------------------- a projection summed in its blocks
 //
 // A linear projection (the up projection, the shared expert's down
-// projection) for up to 16 tokens in one launch: a block holds every K split
+// projection) for up to 32 tokens in one launch: a block holds every K split
 // of its row tiles, one consumer wave per (tile, split) over the plan's K
 // range of that split.  So each wave's FP32 sum is, bit for bit, the split
 // partial the streamed kernel writes (the same MFMAs on the same operands in
@@ -1383,28 +1411,17 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
   lds_barrier();
 
   if (wave == kLocalWaves) {
-    // The producer: chunk x once every consumer is past chunk x - kRing.  A
-    // block stages the activations of all its K ranges (half as many bytes
-    // as its weights at 16 tokens), so two chunks stay in flight: chunk x - 1
-    // is published once chunk x's loads are out and x - 1's have landed
-    // (direct loads complete in order: at most chunk x's kStreamLoads left).
+    // The producer, as the streamed kernel's (two chunks in flight): a block
+    // stages the activations of all its K ranges, half as many bytes as its
+    // weights at 16 tokens and as many at 32.
     for (int x = 1; x < nchunks; ++x) {
-      if (x >= kRing) {
-        const int need = x - kRing + 1;
-        for (int it = 0; it < kSpinLimit; ++it) {
-          const int v = lane < kLocalWaves ? flag_get(flags + 1 + lane) : need;
-          if (__ballot(v < need) == 0) break;
-          __builtin_amdgcn_s_sleep(1);
-        }
-        asm volatile("" ::: "memory");
-      }
+      if (x >= kRing) producer_wait<kLocalWaves>(flags, x - kRing + 1);
       local_issue<NT, kS>(a, xs, x);
-      static_assert(kStreamLoads == 32, "the wait below counts one chunk's loads");
       asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-      if (lane == 0) flag_set(flags, x);
+      if (lane == 0) producer_flag_set(flags, x);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0) flag_set(flags, nchunks);
+    if (lane == 0) producer_flag_set(flags, nchunks);
   } else {
     const int tau = wave / kS, split = wave - tau * kS;
     const int tile = pos * kT + tau;
@@ -2291,24 +2308,21 @@ hipError_t local_launch(const LocalArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The streamed plans whose K splits one block holds: one token block, and
-// 4 splits (2 row tiles a block: 224 blocks for 7168 rows) or 8.  A block
-// stages the activations of all its K ranges, half its weight bytes at 16
-// tokens and as many at 32, where the split-K launch stages 0.29 of them:
-// measured at 32 tokens the block-local launch ran 2.2 us (up projection)
-// and 3.9 us (down projection) longer than the split-K launch, more than
-// the sum launch it saves.  Other plans keep the split-K launch and its sum
-// launch.
+// The streamed plans whose K splits one block holds: 4 splits (2 row tiles
+// a block: 224 blocks for 7168 rows) up to 32 tokens, or 8 at one token
+// block.  Other plans keep the split-K launch and its sum launch.
 bool linear_local(int b, const ProjPlan& p) {
-  return p.stream && p.passes <= 1 && token_blocks(b) == 1 && (p.splits == 4 || p.splits == 8);
+  if (!p.stream || p.passes > 1) return false;
+  const int nt = token_blocks(b);
+  return (p.splits == 4 && nt <= 2) || (p.splits == 8 && nt == 1);
 }
 
 hipError_t local_dispatch(const LocalArgs& a, const ProjPlan& p, hipStream_t s) {
-  if (token_blocks(a.b) != 1) return hipErrorInvalidValue;  // not a shape linear_local takes
-  switch (p.splits) {
-    case 4: return local_launch<1, 4>(a, s);
-    case 8: return local_launch<1, 8>(a, s);
-    default: return hipErrorInvalidValue;
+  switch (token_blocks(a.b) * 10 + p.splits) {
+    case 14: return local_launch<1, 4>(a, s);
+    case 18: return local_launch<1, 8>(a, s);
+    case 24: return local_launch<2, 4>(a, s);
+    default: return hipErrorInvalidValue;  // not a shape linear_local takes
   }
 }
 

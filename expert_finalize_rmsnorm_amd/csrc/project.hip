@@ -902,16 +902,20 @@ __device__ __forceinline__ void px_body_stream(const FxArgs& a0, const FxArgs& a
   // first ring loads (12 MB over the grid) would otherwise fill the memory
   // queues ahead of them, and every consumer waits for that chunk (measured:
   // it arrived 2.6-3.5 us into the launch).  Issued, then the block meets at
-  // an LDS-only barrier (the flags set; no wait for memory).
-  if (wave == kW && nchunks > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, 0);
+  // an LDS-only barrier (the flags set; no wait for memory).  The producer
+  // meets it at a barrier of its own: no code path of the other waves passes
+  // its direct loads, which would make the compiler wait for all of their
+  // ring loads before their first LDS access.
+  if (wave == kW) {
+    if (nchunks > 0) stream_issue<NT, kPhases>(ph0, ph1, xs, 0);
+    lds_barrier();
+    stream_producer<NT, kW, kPhases>(ph0, ph1, xs, flags, nchunks);
+    return;
+  }
   lds_barrier();
   if (kFuse == kFuseGateUp && wave == kW + 1) {
     if (f.lat)
       for (int t = blockIdx.x; t < a0.b; t += gridDim.x) latent_norm_wave(f, a0.b, t);
-    return;
-  }
-  if (wave == kW) {
-    stream_producer<NT, kW, kPhases>(ph0, ph1, xs, flags, nchunks);
     return;
   }
   STREAM_LOCALS(A0)
@@ -1407,10 +1411,12 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
   const int kr = a.k_per_split;
   const int nchunks = (kr + kc - 1) / kc;  // split 0's range is the longest
   if (threadIdx.x < 1 + kLocalWaves) flag_set(flags + threadIdx.x, 0);
-  if (wave == kLocalWaves) local_issue<NT, kS>(a, xs, 0);
-  lds_barrier();
-
+  // (the producer's code and the consumers' meet only at the final barrier:
+  // a consumer path through the direct loads would make the compiler wait
+  // for every ring load before each chunk's flag poll)
   if (wave == kLocalWaves) {
+    local_issue<NT, kS>(a, xs, 0);
+    lds_barrier();
     // The producer, as the streamed kernel's (two chunks in flight): a block
     // stages the activations of all its K ranges, half as many bytes as its
     // weights at 16 tokens and as many at 32.
@@ -1423,6 +1429,7 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0) producer_flag_set(flags, nchunks);
   } else {
+    lds_barrier();
     const int tau = wave / kS, split = wave - tau * kS;
     const int tile = pos * kT + tau;
     const int kb0 = split * kr;

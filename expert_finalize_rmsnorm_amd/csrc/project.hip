@@ -1337,7 +1337,7 @@ __global__ void __launch_bounds__(256) tail_out_kernel(const f32x4_t* down_parti
 // --------------------------------------- a projection summed in its blocks
 //
 // A linear projection (the up projection, the shared expert's down
-// projection) for up to 32 tokens in one launch: a block holds every K split
+// projection) for up to 64 tokens in one launch: a block holds every K split
 // of its row tiles, one consumer wave per (tile, split) over the plan's K
 // range of that split.  So each wave's FP32 sum is, bit for bit, the split
 // partial the streamed kernel writes (the same MFMAs on the same operands in
@@ -1359,12 +1359,18 @@ struct LocalArgs {
 };
 
 // Columns of one split's sub-chunk: NT token blocks x kLocalCols fill the
-// chunk with kS sub-chunks; at least 16 pieces of 8 a row, so the piece
-// swizzle (piece ^ row) stays inside the row.
+// chunk with kS sub-chunks.  A row's pieces of 8 are swizzled by the row
+// (piece ^ row) over 16 pieces, or over the 8 of a 64-column row (4 token
+// blocks: the 16 rows of an operand read then meet in pairs on the LDS
+// banks, which measured neutral there).
 template <int NT, int kS>
 constexpr int kLocalCols = kStreamCols<NT> / kS;
+template <int NT, int kS>
+constexpr int kLocalSwz = (kLocalCols<NT, kS> / 8 >= 16) ? 15 : (kLocalCols<NT, kS> / 8 - 1);
+// Up to 2 token blocks the waves' sums have LDS of their own beside the
+// ring; at 4 (32 KB of sums) they go into the ring once it is free.
 template <int NT>
-constexpr int kLocalLds = kRing * kStreamChunkBytes + 256 + kLocalWaves * NT * kWave * 16;
+constexpr int kLocalLds = kRing * kStreamChunkBytes + 256 + (NT <= 2 ? kLocalWaves * NT * kWave * 16 : 0);
 
 // Chunk x's activations for every split into its ring buffer (not waited
 // for): sub-chunk q holds token rows 0 .. 16 NT - 1 of columns
@@ -1384,7 +1390,7 @@ __device__ __forceinline__ void local_issue(const LocalArgs& a, uint16_t* xs, in
     const int q = e / kSub;
     const int rem = e - q * kSub;
     const int t = rem / kc;
-    const int piece = ((rem - t * kc) >> 3) ^ (t & 15);
+    const int piece = ((rem - t * kc) >> 3) ^ (t & kLocalSwz<NT, kS>);
     const int col = min(q * a.k_per_split + x * kc + 8 * piece, a.K - 8);
     const uint16_t* g = a.X + (int64_t)min(t, a.b - 1) * a.K + col;
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)(buf + j * 512), 16, 0, 0);
@@ -1393,7 +1399,8 @@ __device__ __forceinline__ void local_issue(const LocalArgs& a, uint16_t* xs, in
 
 template <int NT, int kS, int kPF>
 __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(LocalArgs a) {
-  static_assert(kLocalWaves % kS == 0 && kLocalCols<NT, kS> >= 128, "sub-chunk shape");
+  static_assert(kLocalWaves % kS == 0 && kLocalCols<NT, kS> >= 64, "sub-chunk shape");
+  static_assert(kLocalWaves * NT * kWave * 16 <= kRing * kStreamChunkBytes, "sums in the ring");
   constexpr int kT = kLocalWaves / kS;     // row tiles a block
   constexpr int kc = kLocalCols<NT, kS>;
   constexpr int kSpc = kc / kKStep;        // k steps of a sub-chunk
@@ -1401,7 +1408,8 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
   constexpr int kChunkElems = kStreamChunkBytes / 2;
   extern __shared__ uint16_t xs[];
   int* flags = reinterpret_cast<int*>(xs + kRing * kChunkElems);
-  f32x4_t* sums = reinterpret_cast<f32x4_t*>(xs + kRing * kChunkElems + 128);
+  f32x4_t* sums = NT <= 2 ? reinterpret_cast<f32x4_t*>(xs + kRing * kChunkElems + 128)
+                          : reinterpret_cast<f32x4_t*>(xs);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lrow = lane & 15;
@@ -1419,7 +1427,7 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
     lds_barrier();
     // The producer, as the streamed kernel's (two chunks in flight): a block
     // stages the activations of all its K ranges, half as many bytes as its
-    // weights at 16 tokens and as many at 32.
+    // weights at 16 tokens, as many at 32 and twice as many at 64.
     for (int x = 1; x < nchunks; ++x) {
       if (x >= kRing) producer_wait<kLocalWaves>(flags, x - kRing + 1);
       local_issue<NT, kS>(a, xs, x);
@@ -1459,7 +1467,8 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
             const int cx = st / kSpc, ci = st - cx * kSpc;
             if (ci == 0) wait_filled(flags, cx + 1);
             const uint16_t* xp =
-                xs + (cx % kRing) * kChunkElems + xoff + (((4 * ci + kq) ^ lrow) << 3);
+                xs + (cx % kRing) * kChunkElems + xoff +
+                (((4 * ci + kq) ^ (lrow & kLocalSwz<NT, kS>)) << 3);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
               const uint4 bq = *reinterpret_cast<const uint4*>(xp + 16 * nt * kc);
@@ -1477,9 +1486,13 @@ __global__ void __launch_bounds__(kWave * (kLocalWaves + 1)) px_local_kernel(Loc
         }
       }
     }
+    // at 4 token blocks the sums go into the ring, free once every wave has
+    // met here (the producer meets this barrier below)
+    if (NT > 2) lds_barrier();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sums[(wave * NT + nt) * kWave + lane] = acc[nt];
   }
+  if (NT > 2 && wave == kLocalWaves) lds_barrier();
   lds_barrier();
 
   // Output tile tau's token block nt on wave tau NT + nt: the splits' sums in
@@ -2316,12 +2329,12 @@ hipError_t local_launch(const LocalArgs& a, hipStream_t s) {
 }
 
 // The streamed plans whose K splits one block holds: 4 splits (2 row tiles
-// a block: 224 blocks for 7168 rows) up to 32 tokens, or 8 at one token
+// a block: 224 blocks for 7168 rows) up to 64 tokens, or 8 at one token
 // block.  Other plans keep the split-K launch and its sum launch.
 bool linear_local(int b, const ProjPlan& p) {
   if (!p.stream || p.passes > 1) return false;
   const int nt = token_blocks(b);
-  return (p.splits == 4 && nt <= 2) || (p.splits == 8 && nt == 1);
+  return (p.splits == 4 && nt <= 4) || (p.splits == 8 && nt == 1);
 }
 
 hipError_t local_dispatch(const LocalArgs& a, const ProjPlan& p, hipStream_t s) {
@@ -2329,6 +2342,7 @@ hipError_t local_dispatch(const LocalArgs& a, const ProjPlan& p, hipStream_t s) 
     case 14: return local_launch<1, 4>(a, s);
     case 18: return local_launch<1, 8>(a, s);
     case 24: return local_launch<2, 4>(a, s);
+    case 44: return local_launch<4, 4>(a, s);
     default: return hipErrorInvalidValue;  // not a shape linear_local takes
   }
 }

@@ -1041,12 +1041,13 @@ def test_projection_partials_are_the_shared_experts():
 @pytest.mark.parametrize("b,L,N,layout", [(32, 3584, 7168, mt.W_TILED), (17, 3584, 7168, mt.W_ROWS),
                                           (9, 3584, 7168, mt.W_ROWS), (1, 3584, 7168, mt.W_TILED),
                                           (32, 3616, 7168, mt.W_TILED), (5, 128, 256, mt.W_ROWS),
-                                          (20, 128, 256, mt.W_TILED), (64, 3584, 7168, mt.W_TILED)])
+                                          (20, 128, 256, mt.W_TILED), (64, 3584, 7168, mt.W_TILED),
+                                          (50, 3616, 7168, mt.W_ROWS), (40, 128, 256, mt.W_TILED)])
 def test_upproj_block_sums_are_the_split_k_stage(b, L, N, layout):
-    """Up to 32 tokens the up projection adds its K splits inside its blocks
-    (one launch after the norm); above, a split-K launch and a sum launch.
-    Either way its out is, bit for bit, the split-K stage's partials of the
-    same y added in split order from +0, plus rs, rounded once (-0 as +0).
+    """Up to 64 tokens the up projection adds its K splits inside its blocks
+    (one launch after the norm).  Its out is, bit for bit, the split-K
+    stage's partials of the same y added in split order from +0, plus rs,
+    rounded once (-0 as +0).
     L = 3616: 4 splits of 928 columns, the last one shorter; 128 -> 256: 4
     splits of one k step."""
     up = workloads.upproj(90 + b, b=b, L=L, N=N, with_rs=True)
@@ -1067,9 +1068,9 @@ def test_upproj_block_sums_are_the_split_k_stage(b, L, N, layout):
     assert np.array_equal(oracle.bf16_round(acc), host(out))
 
 
-@pytest.mark.parametrize("b", [1, 11, 20, 32, 64])
+@pytest.mark.parametrize("b", [1, 11, 20, 32, 50, 64, 100])
 def test_shared_down_block_sums_are_the_split_k_stage(b):
-    """The shared expert's down projection (summed inside its blocks up to 32
+    """The shared expert's down projection (summed inside its blocks up to 64
     tokens): rs is, bit for bit, the split-K stage's partials of the same h
     added in split order from +0 and rounded once (-0 as +0)."""
     sh = workloads.shared(95 + b, b=b)

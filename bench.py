@@ -69,7 +69,7 @@ def graph_steps(steps: int) -> int:
 # kernel (256 MiB in, 256 MiB out: FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # They hold for the kernel sources with this digest only (None: not taken
 # for these sources).
-TRAFFIC = dict(source_digest="c5c7eaa56613f13e", fetch_bytes=93310 * 2 * 1024,
+TRAFFIC = dict(source_digest="1d2d1e8c1dd4ef36", fetch_bytes=93308 * 2 * 1024,
                write_bytes=7420 * 1024)
 
 

@@ -281,8 +281,8 @@ int moetail_gate_up(const uint16_t* x, int b, int H, const uint16_t* w_gate,
  *     out = moetail_combine_norm_upproj(latent_partials, rs) (as that call)
  * with the hidden width H as the up projection's output width N.  The
  * results are the same bits as those two calls in that order.  With the
- * library's own (streamed) plans the work is two launches instead of seven:
- * gate/up forming h in the launch, beside y; then the down and up
+ * library's own (streamed) plans the work is two launches (the two calls
+ * take five to seven): gate/up forming h in the launch, beside y; then the down and up
  * projections as one grid forming rs and out in the launch.  (With plan
  * overrides that select other kernels: four launches, gate/up; {h, y};
  * {down, up}; {rs, out}.)
@@ -320,8 +320,8 @@ int moetail_tail(const uint16_t* latent_partials, int tp, const uint16_t* gamma,
  *     out             = moetail_tail(latent_partials, ...)
  * with the finalize's width P equal to the latent width L.  The results are
  * the same bits as those two calls in that order (latent_partials is
- * written, the resident rank-partial buffer): five launches, every argument
- * of both checked before the first.
+ * written, the resident rank-partial buffer): three launches with the
+ * library's own plans, every argument of both checked before the first.
  *
  *   rows .. K        as in moetail_finalize (fin_gamma, fin_eps: its gamma
  *                    [L] and eps; weight_before_norm: its norm mode).
